@@ -1,0 +1,23 @@
+"""Plain, slow, fp64 CPU oracle of fine-grained (Mx1-slice / column-sparse) attention.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or call anything in this package.  The library
+path (sparse_self_attention_amd) never imports it, and the oracle imports
+nothing from the library: the two share no code.
+
+Every function states the passage of the pages it follows (page title plus the
+section, figure or comment it falls in).
+
+Readings of passages that the pages leave open:
+  * attention is scaled dot-product with scale = 1/sqrt(D), non-causal, no bias;
+  * the sparse forward renormalises over the kept keys only (the restricted
+    softmax, not a masked full softmax);
+  * the pooling threshold "exp(k . q_avg / sqrt D) / D < tau" is read with D as
+    the lost softmax denominator: a key is skipped when its pooled softmax
+    probability is below tau;
+  * a group with no kept keys outputs zeros and lse = -inf;
+  * top-k ties go to the lowest key index; index lists are ascending.
+"""
+from .attention import dense_attention_ref, sparse_attention_ref, sparse_attention_probs_ref  # noqa: F401
+from .mask import (group_mean_ref, group_scores_ref, topk_select_ref, thresh_select_ref,  # noqa: F401
+                   mask_ref)

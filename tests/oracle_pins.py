@@ -1,0 +1,268 @@
+"""Checks that pin the oracle to facts other than itself.
+
+Each check takes the implementation under test as an argument, so the same
+check runs against the real oracle (tests/test_oracle_*.py) and against copies
+with a planted mistake (tests/test_oracle_mutants.py), which must fail at
+least one check.  A check raises AssertionError on failure.
+
+Sources of truth used here, none of which is the oracle's own code:
+  * an independent library routine (torch's CPU scaled_dot_product_attention
+    in float64, scipy's logsumexp) for the case where every key is kept;
+  * a separately written gather-based loop with math.fsum / math.exp;
+  * closed forms (Q = 0, one kept key, constant V, key shift, huge logits);
+  * invariants (rows sum to 1, zero off the mask, convex hull, ones column);
+  * brute-force rank counting for top-k and explicit probabilities for the
+    threshold cut.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOL = 1e-12
+
+
+# ----------------------------------------------------------------------------
+# forward
+# ----------------------------------------------------------------------------
+
+def _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=1.0):
+    q = rng.standard_normal((B, H, Nq, D)) * scale_q
+    k = rng.standard_normal((B, H, Nk, D))
+    v = rng.standard_normal((B, H, Nk, D))
+    return q, k, v
+
+
+def _random_lists(rng, B, H, G, Nk, cap, min_c=1):
+    counts = rng.integers(min_c, cap + 1, size=(B, H, G)).astype(np.int32)
+    idx = np.full((B, H, G, cap), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                c = counts[b, h, g]
+                idx[b, h, g, :c] = np.sort(rng.choice(Nk, size=c, replace=False))
+    return idx, counts
+
+
+def check_all_keys_equals_library(fwd):
+    """Every key kept => plain softmax attention, computed by torch SDPA (CPU, float64)."""
+    import torch
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(11)
+    for (B, H, Nq, Nk, D, M) in [(1, 2, 37, 29, 8, 16), (2, 1, 20, 45, 16, 4), (1, 1, 9, 9, 4, 1)]:
+        q, k, v = _rand_qkv(rng, B, H, Nq, Nk, D)
+        scale = 1.0 / math.sqrt(D)
+        G = -(-Nq // M)
+        idx = np.broadcast_to(np.arange(Nk, dtype=np.int32), (B, H, G, Nk)).copy()
+        counts = np.full((B, H, G), Nk, dtype=np.int32)
+        out, lse = fwd(q, k, v, idx, counts, M, scale)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=scale).numpy()
+        assert np.abs(out - ref).max() <= TOL, "all-keys forward differs from SDPA"
+        S = np.stack([[q[b, h] @ k[b, h].T for h in range(H)] for b in range(B)]) * scale
+        assert np.abs(lse - logsumexp(S, axis=-1)).max() <= TOL, "all-keys lse differs from logsumexp"
+
+
+def _brute_force_unit(q, k, v, J, rows, scale):
+    out, lse = [], []
+    for i in rows:
+        s = [scale * math.fsum(float(q[i, d]) * float(k[j, d]) for d in range(q.shape[1])) for j in J]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        l = math.fsum(w)
+        out.append([math.fsum(w[t] * float(v[J[t], d]) for t in range(len(J))) / l for d in range(v.shape[1])])
+        lse.append(m + math.log(l))
+    return np.array(out), np.array(lse)
+
+
+def check_brute_force_tiny(fwd):
+    """Explicit gather over the kept list with math.fsum, tiny shapes, partial groups, random lists."""
+    rng = np.random.default_rng(12)
+    for (B, H, Nq, Nk, D, M) in [(1, 2, 13, 17, 4, 4), (1, 1, 40, 23, 8, 16), (1, 2, 7, 11, 3, 1),
+                                 (1, 1, 33, 40, 5, 16)]:
+        q, k, v = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=2.0)
+        G = -(-Nq // M)
+        cap = min(Nk, 9)
+        idx, counts = _random_lists(rng, B, H, G, Nk, cap)
+        scale = 0.7 / math.sqrt(D)
+        out, lse = fwd(q, k, v, idx, counts, M, scale)
+        for b in range(B):
+            for h in range(H):
+                for g in range(G):
+                    rows = range(g * M, min((g + 1) * M, Nq))
+                    J = [int(j) for j in idx[b, h, g, :counts[b, h, g]]]
+                    o_ref, l_ref = _brute_force_unit(q[b, h], k[b, h], v[b, h], J, rows, scale)
+                    assert np.abs(out[b, h, list(rows)] - o_ref).max() <= TOL, "brute-force output mismatch"
+                    assert np.abs(lse[b, h, list(rows)] - l_ref).max() <= TOL, "brute-force lse mismatch"
+
+
+def check_closed_forms(fwd):
+    """Q = 0; a single kept key; constant V; key shift; permuted list order; huge logits."""
+    rng = np.random.default_rng(13)
+    B, H, Nq, Nk, D, M = 1, 2, 24, 30, 6, 8
+    G = Nq // M
+    q, k, v = _rand_qkv(rng, B, H, Nq, Nk, D)
+    idx, counts = _random_lists(rng, B, H, G, Nk, 12, min_c=2)
+    scale = 1.0 / math.sqrt(D)
+    # Q = 0: every kept key has score 0 -> out = mean of kept V rows, lse = ln c
+    out, lse = fwd(np.zeros_like(q), k, v, idx, counts, M, scale)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                J = idx[b, h, g, :counts[b, h, g]]
+                rows = slice(g * M, (g + 1) * M)
+                assert np.abs(out[b, h, rows] - v[b, h, J].mean(axis=0)).max() <= TOL, "Q=0: out != mean(V[J])"
+                assert np.abs(lse[b, h, rows] - math.log(len(J))).max() <= TOL, "Q=0: lse != ln c"
+    # one kept key j: out = v_j, lse = scale q_i . k_j
+    one_idx = idx[..., :1].copy()
+    one_cnt = np.ones_like(counts)
+    out, lse = fwd(q, k, v, one_idx, one_cnt, M, scale)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                j = one_idx[b, h, g, 0]
+                rows = slice(g * M, (g + 1) * M)
+                assert np.abs(out[b, h, rows] - v[b, h, j]).max() <= TOL, "one key: out != v_j"
+                assert np.abs(lse[b, h, rows] - scale * q[b, h, rows] @ k[b, h, j]).max() <= TOL, "one key: lse"
+    # constant V rows -> out = that row
+    vc = np.broadcast_to(rng.standard_normal(D), v.shape).copy()
+    out, _ = fwd(q, k, vc, idx, counts, M, scale)
+    assert np.abs(out - vc[:, :, :1]).max() <= 1e-12, "constant V: out != v"
+    # K_j -> K_j + u for all j: out unchanged, lse += scale q_i . u
+    u = rng.standard_normal(D)
+    out0, lse0 = fwd(q, k, v, idx, counts, M, scale)
+    out1, lse1 = fwd(q, k + u, v, idx, counts, M, scale)
+    assert np.abs(out1 - out0).max() <= 1e-11, "key shift changed out"
+    assert np.abs(lse1 - lse0 - scale * (q @ u)).max() <= 1e-11, "key shift: lse shift != scale q.u"
+    # order of a group's list does not matter
+    perm_idx = idx.copy()
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                c = counts[b, h, g]
+                perm_idx[b, h, g, :c] = perm_idx[b, h, g, :c][::-1]
+    out2, lse2 = fwd(q, k, v, perm_idx, counts, M, scale)
+    assert np.abs(out2 - out0).max() <= TOL and np.abs(lse2 - lse0).max() <= TOL, "list order changed result"
+    # logits far beyond the fp32 exp range (LongLive blog, "Online Softmax": e^S overflows fp32 past 88):
+    # two keys with scores 1000 and 1000 + ln 3 give weights 1/4 and 3/4 exactly.
+    qq = np.zeros((1, 1, 1, 2)); qq[0, 0, 0] = [1.0, 0.0]
+    kk = np.array([[[[1000.0, 0.0], [1000.0 + math.log(3.0), 0.0]]]])
+    vv = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    out, lse = fwd(qq, kk, vv, np.array([[[[0, 1]]]], dtype=np.int32), np.array([[[2]]], dtype=np.int32), 1, 1.0)
+    assert abs(out[0, 0, 0, 0] - 0.25) <= TOL and abs(out[0, 0, 0, 1] - 0.75) <= TOL, "huge logits: weights"
+    assert abs(lse[0, 0, 0] - (1000.0 + math.log(4.0))) <= 1e-9, "huge logits: lse"
+
+
+def check_invariants(fwd, probs):
+    """Rows sum to 1 over the kept keys, zero elsewhere; convex hull; ones column; empty group."""
+    rng = np.random.default_rng(14)
+    B, H, Nq, Nk, D, M = 1, 2, 21, 26, 5, 8
+    G = -(-Nq // M)
+    q, k, v = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=3.0)
+    idx, counts = _random_lists(rng, B, H, G, Nk, 10)
+    scale = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                P, _ = probs(q, k, idx, counts, M, scale, b, h, g)
+                J = idx[b, h, g, :counts[b, h, g]]
+                off = np.ones(Nk, dtype=bool); off[J] = False
+                assert np.abs(P.sum(axis=1) - 1.0).max() <= TOL, "probability rows do not sum to 1"
+                assert np.all(P[:, off] == 0.0), "probability on an unselected key"
+                assert np.all(P[:, J] > 0.0), "kept key with zero probability"
+    vo = v.copy(); vo[..., 0] = 1.0
+    out, _ = fwd(q, k, vo, idx, counts, M, scale)
+    assert np.abs(out[..., 0] - 1.0).max() <= TOL, "ones column of V does not map to 1"
+    out, _ = fwd(q, k, v, idx, counts, M, scale)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                J = idx[b, h, g, :counts[b, h, g]]
+                rows = slice(g * M, min((g + 1) * M, Nq))
+                lo, hi = v[b, h, J].min(axis=0), v[b, h, J].max(axis=0)
+                assert np.all(out[b, h, rows] >= lo - TOL) and np.all(out[b, h, rows] <= hi + TOL), "convex hull"
+    # a group with no kept key: out = 0, lse = -inf
+    counts0 = counts.copy(); counts0[0, 1, 1] = 0
+    out, lse = fwd(q, k, v, idx, counts0, M, scale)
+    rows = slice(M, 2 * M)
+    assert np.all(out[0, 1, rows] == 0.0) and np.all(np.isneginf(lse[0, 1, rows])), "empty group"
+
+
+# ----------------------------------------------------------------------------
+# mask
+# ----------------------------------------------------------------------------
+
+def check_group_mean(group_mean):
+    rng = np.random.default_rng(21)
+    row = rng.standard_normal(7)
+    q = np.broadcast_to(row, (1, 1, 20, 7)).copy()
+    assert np.abs(group_mean(q, 8) - row).max() <= TOL, "identical rows: mean != row"
+    # rows 1..20 in channel 0: groups of 8 -> means 4.5, 12.5 and (17+..+20)/4 = 18.5 (true tail size)
+    q = np.zeros((1, 1, 20, 2)); q[0, 0, :, 0] = np.arange(1, 21)
+    m = group_mean(q, 8)[0, 0, :, 0]
+    assert np.allclose(m, [4.5, 12.5, 18.5], rtol=0, atol=TOL), "group means (tail divides by its true size)"
+    q = rng.standard_normal((1, 2, 5, 3))
+    assert np.abs(group_mean(q, 1) - q).max() <= TOL, "M=1: mean != the query"
+
+
+def check_group_scores(scores):
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((1, 2, 6, 5)); k = rng.standard_normal((1, 2, 9, 5))
+    s = scores(q, k, 1, 0.3)
+    for h in range(2):
+        for i in range(6):
+            for j in range(9):
+                ref = 0.3 * math.fsum(q[0, h, i, d] * k[0, h, j, d] for d in range(5))
+                assert abs(s[0, h, i, j] - ref) <= TOL, "M=1 scores != scale q_i.k_j"
+    s = scores(q, k, 4, 0.3)   # groups rows 0..3 and 4..5
+    for h in range(2):
+        for j in range(9):
+            ref0 = 0.3 * math.fsum(q[0, h, i, d] * k[0, h, j, d] for i in range(4) for d in range(5)) / 4
+            ref1 = 0.3 * math.fsum(q[0, h, i, d] * k[0, h, j, d] for i in range(4, 6) for d in range(5)) / 2
+            assert abs(s[0, h, 0, j] - ref0) <= TOL and abs(s[0, h, 1, j] - ref1) <= TOL, "group scores"
+
+
+def check_topk(topk_select):
+    rng = np.random.default_rng(23)
+    for n, kk in [(50, 7), (33, 1), (20, 20), (64, 16)]:
+        s = rng.standard_normal(n)
+        s[rng.integers(0, n, 5)] = s[3]                      # plant ties
+        kept, t = topk_select(s, kk)
+        brute = [j for j in range(n)
+                 if sum(1 for i in range(n) if s[i] > s[j] or (s[i] == s[j] and i < j)) < kk]
+        assert list(kept) == brute, "top-k set != brute-force rank set (ties to lower index)"
+        assert len(kept) == kk and np.all(np.diff(kept) > 0), "top-k count / ascending order"
+        dropped = np.setdiff1d(np.arange(n), kept)
+        if dropped.size:
+            assert s[kept].min() >= s[dropped].max(), "a dropped score beats a kept one"
+        assert t == s[kept].min(), "boundary score != smallest kept score"
+    kept, _ = topk_select(rng.standard_normal(12), 12)
+    assert list(kept) == list(range(12)), "k = N must keep every key"
+    s = np.zeros(10)
+    kept, _ = topk_select(s, 3)
+    assert list(kept) == [0, 1, 2], "all-equal scores: lowest indices win"
+
+
+def check_thresh(thresh_select):
+    rng = np.random.default_rng(24)
+    for n in (17, 64):
+        s = rng.standard_normal(n) * 3
+        l = math.fsum(math.exp(x) for x in s)
+        p = [math.exp(x) / l for x in s]
+        kept, _ = thresh_select(s, 0.0)
+        assert list(kept) == list(range(n)), "tau = 0 must keep every key"
+        for tau in (0.5 / n, 1.0 / n, 2.0 / n, 0.05):
+            kept, t = thresh_select(s, tau)
+            ks = set(int(j) for j in kept)
+            if max(p) < tau:
+                assert ks == {int(np.argmax(s))}, "no key reaches the cut: keep the arg-max only"
+                continue
+            for j in range(n):
+                if abs(p[j] - tau) > 1e-12 * tau:
+                    assert (j in ks) == (p[j] >= tau), "threshold cut disagrees with explicit probabilities"
+        kept, _ = thresh_select(s, max(p) * 1.5)
+        assert list(kept) == [int(np.argmax(s))], "cut above every p: keep the arg-max only"
+    s = np.array([1.0, 3.0, 3.0, 2.0])
+    kept, _ = thresh_select(s, 0.99)
+    assert list(kept) == [1], "arg-max fallback: lowest index on ties"

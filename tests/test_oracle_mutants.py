@@ -1,0 +1,88 @@
+"""Each copy of the oracle with one planted mistake must fail at least one pin.
+
+The mutants are built on the CPU from the oracle's own source text with a
+single textual change, executed in a fresh namespace.  This shows that the pins
+in oracle_pins.py would catch a dropped term, a wrong sign or index, or a
+transposed or swapped operand in the oracle.
+"""
+import importlib
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+
+
+def _mutant(modname, old, new):
+    mod = importlib.import_module(modname)
+    src = inspect.getsource(mod)
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new, 1)
+    m = types.ModuleType(modname + "_mutant")
+    m.__dict__["__name__"] = modname + "_mutant"
+    exec(compile(src, modname + "_mutant", "exec"), m.__dict__)
+    return m
+
+
+def _caught(checks):
+    for check in checks:
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except Exception:     # an assertion or a crash both expose the mutant
+            return True
+    return False
+
+
+FWD_MUTANTS = [
+    ("scale dropped", "S = (q[b, h, r0:r1] @ k[b, h].T) * scale", "S = (q[b, h, r0:r1] @ k[b, h].T)"),
+    ("masked full softmax (no renormalisation)",
+     "S[:, ~keep] = -np.inf\n    P, lse = _softmax_rows(S)",
+     "P, lse = _softmax_rows(S)\n    P[:, ~keep] = 0.0"),
+    ("no max subtraction", "E = np.exp(S - m_safe)", "E = np.exp(S)"),
+    ("lse without the max term", "m_safe[:, 0] + np.log(", "np.log("),
+    ("softmax over the wrong axis", "m = S.max(axis=1, keepdims=True)", "m = S.max(axis=0, keepdims=True)"),
+    ("keys reversed (wrong index)", "S = (q[b, h, r0:r1] @ k[b, h].T)", "S = (q[b, h, r0:r1] @ k[b, h][::-1].T)"),
+    ("last kept key dropped", "J = np.asarray(idx[b, h, g, :c], dtype=np.int64)",
+     "J = np.asarray(idx[b, h, g, :max(c - 1, 1)], dtype=np.int64)"),
+    ("group rows shifted", "r0, r1 = g * group, min((g + 1) * group, Nq)\n    c =",
+     "r0, r1 = max(g * group - 1, 0), min((g + 1) * group, Nq) - (1 if g else 0)\n    c ="),
+    ("V rows reversed", "out[b, h, r0:r1] = P @ v[b, h]", "out[b, h, r0:r1] = P @ v[b, h][::-1]"),
+    ("wrong sign in exponent", "E = np.exp(S - m_safe)", "E = np.exp(m_safe - S)"),
+]
+
+MASK_MUTANTS = [
+    ("tail mean divides by M", "out[:, :, g] = q[:, :, r0:r1].sum(axis=2) / (r1 - r0)",
+     "out[:, :, g] = q[:, :, r0:r1].sum(axis=2) / group"),
+    ("score scale dropped", 'return np.einsum("bhgd,bhnd->bhgn", qm, k) * scale',
+     'return np.einsum("bhgd,bhnd->bhgn", qm, k)'),
+    ("top-k ties to the higher index", "np.lexsort((np.arange(n), -s_row))", "np.lexsort((-np.arange(n), -s_row))"),
+    ("top-k keeps one too few", "kept = order[:topk]", "kept = order[:max(topk - 1, 1)]"),
+    ("top-k keeps the lowest scores", "np.lexsort((np.arange(n), -s_row))", "np.lexsort((np.arange(n), s_row))"),
+    ("threshold with the wrong sign of ln tau", "lse + math.log(tau)", "lse - math.log(tau)"),
+    ("lse without the max term", "lse = m + math.log(", "lse = math.log("),
+    ("fallback keeps the arg-min", "kept = np.array([int(np.argmax(s_row))])", "kept = np.array([int(np.argmin(s_row))])"),
+    ("mean over the wrong axis", "q[:, :, r0:r1].sum(axis=2)", "q[:, :, r0:r1].sum(axis=3, keepdims=False)[..., None]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", FWD_MUTANTS, ids=[m[0] for m in FWD_MUTANTS])
+def test_forward_mutant_is_caught(name, old, new):
+    m = _mutant("oracle.attention", old, new)
+    checks = [lambda: pins.check_all_keys_equals_library(m.sparse_attention_ref),
+              lambda: pins.check_brute_force_tiny(m.sparse_attention_ref),
+              lambda: pins.check_closed_forms(m.sparse_attention_ref),
+              lambda: pins.check_invariants(m.sparse_attention_ref, m.sparse_attention_probs_ref)]
+    assert _caught(checks), f"no pin catches the planted mistake: {name}"
+
+
+@pytest.mark.parametrize("name,old,new", MASK_MUTANTS, ids=[m[0] for m in MASK_MUTANTS])
+def test_mask_mutant_is_caught(name, old, new):
+    m = _mutant("oracle.mask", old, new)
+    checks = [lambda: pins.check_group_mean(m.group_mean_ref),
+              lambda: pins.check_group_scores(m.group_scores_ref),
+              lambda: pins.check_topk(m.topk_select_ref),
+              lambda: pins.check_thresh(m.thresh_select_ref)]
+    assert _caught(checks), f"no pin catches the planted mistake: {name}"
