@@ -1,0 +1,144 @@
+/*
+ * sattn.h - C ABI of the fine-grained (Mx1-slice / column-sparse) self-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major and head-major: Q is [B,H,Nq,D], K and V are [B,H,Nk,D],
+ *    bf16 (IEEE bfloat16 bit patterns, 2 bytes each).  One K or V row is D*2 bytes.
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library never allocates,
+ *    frees or keeps device memory; it only launches kernels on `stream` (a hipStream_t; NULL is
+ *    the default stream) and never synchronises.  Calls are asynchronous: device-side results
+ *    are ready when the stream reaches them.
+ *  - D must be 64 or 128.  Queries are split into G = ceil(Nq / group) groups of `group`
+ *    contiguous tokens; the last group may be partial.  group is a multiple of 16 in [16, 256].
+ *  - scale multiplies q.k before the softmax; pass 1/sqrt(D) for standard attention.
+ *  - Return value: SATTN_OK (0) or a sattn_status code.  Arguments are validated on the host
+ *    before any HIP call; on a validation error nothing is launched and no output is touched.
+ *    A failed launch returns SATTN_ERR_HIP.  Faults inside a kernel surface at the caller's
+ *    next synchronisation.  sattn_last_error() returns a thread-local detail string.
+ *  - Thread safety: every entry point may be called from several host threads at once.
+ */
+#ifndef SATTN_H
+#define SATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SATTN_OK = 0,
+  SATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+  SATTN_ERR_SHAPE = 2,        /* a size is < 1, or sizes overflow the supported index range */
+  SATTN_ERR_UNSUPPORTED = 3,  /* D not in {64,128}; group not a multiple of 16 in [16,256]; Nk too large */
+  SATTN_ERR_ARG = 4,          /* bad mode / dtype / topk / thresh / cap */
+  SATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than sattn_mask_workspace_bytes() */
+  SATTN_ERR_HIP = 6,          /* a HIP launch or runtime call failed */
+  SATTN_ERR_INDEX = 7         /* validation mode: an index list breaks the sattn_forward preconditions */
+} sattn_status;
+
+enum { SATTN_TOPK = 0, SATTN_THRESH = 1 };   /* sattn_mask mode */
+enum { SATTN_BF16 = 0, SATTN_F32 = 1 };      /* output dtype */
+
+/* Largest supported key count for sattn_mask (the per-group scores are held on chip). */
+#define SATTN_MASK_MAX_NK 131072
+
+/*
+ * sattn_mask_workspace_bytes - device workspace that sattn_mask needs for these sizes.
+ * Returns 0 if the sizes are invalid.  The workspace holds the group means and the fp32
+ * mean-query scores of a bounded number of heads at a time.
+ */
+size_t sattn_mask_workspace_bytes(int B, int H, int Nq, int Nk, int D, int group);
+
+/*
+ * sattn_mask - per-group key lists from the group-mean query (the pooling mask).
+ *
+ * FG-Attn review (pith.science/paper/2509.16518), "The pith" and Referee major comment 2:
+ * the queries of a group are averaged into q_avg, every key is scored against it, and slices
+ * whose pooled score is small are skipped.  The threshold there is garbled; it is read as the
+ * pooled softmax probability p_j = exp(s_j) / sum_i exp(s_i), s_j = scale * (q_avg . k_j).
+ * Chipmunk review (pith.science/paper/CJ4ETNKV), "What carries the argument": a top-k index mask.
+ *
+ *   q      bf16 [B,H,Nq,D]            k  bf16 [B,H,Nk,D]
+ *   mode   SATTN_TOPK:   keep the `topk` (1..Nk) highest s_j; ties go to the lower key index.
+ *          SATTN_THRESH: keep j iff p_j >= thresh (thresh in [0,1]; 0 keeps all);
+ *                        if no key qualifies the arg-max key (lowest index on ties) is kept.
+ *   idx    int32 [B,H,G,cap]  out: idx[b,h,g,0:counts[b,h,g]] = kept key indices, strictly
+ *                             ascending; entries past counts are left untouched.
+ *   counts int32 [B,H,G]      out: number kept (= topk in TOPK mode, >= 1 in THRESH mode).
+ *   cap    row length of idx: >= topk (TOPK) or >= Nk (THRESH).
+ *   workspace / ws_bytes: device scratch of at least sattn_mask_workspace_bytes() bytes.
+ * Scores are computed in fp32 (q_avg is split into two bf16 terms for the matrix cores), so a
+ * key whose score lies within ~1e-5 of the cut may land on either side of it.
+ * Errors: SATTN_ERR_NULL, _SHAPE, _UNSUPPORTED (also Nk > SATTN_MASK_MAX_NK), _ARG, _WORKSPACE, _HIP.
+ */
+int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D, int group,
+               int mode, int topk, float thresh, float scale,
+               int32_t* idx, int32_t* counts, int cap,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sattn_forward - fine-grained sparse attention forward over per-group key lists.
+ *
+ * FG-Attn review, "What carries the argument" and Fig. 6 / Fig. 7 captions: each group of
+ * `group` contiguous queries computes scores only against its relevant keys, which are
+ * gathered into dense tiles for the matrix units.  Chipmunk review, Referee major comment 1
+ * (Alg. 3): the softmax is normalised over the selected keys only.  So for group rows R and
+ * kept keys J = idx[b,h,g,0:c], c = counts[b,h,g]:
+ *     out[R] = softmax_J(scale * Q[R] K[J]^T) V[J],   lse[R] = ln sum_{j in J} exp(scale * Q[R].K[j])
+ * computed with bf16 inputs, fp32 accumulation and an fp32 online softmax (LongLive DiT blog,
+ * "Online Softmax").  A group with c = 0 gets out = 0 and lse = -inf.
+ *
+ *   q bf16 [B,H,Nq,D]; k, v bf16 [B,H,Nk,D]
+ *   idx int32 [B,H,G,cap], counts int32 [B,H,G], 0 <= counts <= cap.
+ *   Preconditions: idx[b,h,g,0:counts] unique, ascending, in [0,Nk).  Entries past counts
+ *   are never read.  With the environment variable SATTN_VALIDATE=1 the lists are checked on
+ *   the device first (the call then synchronises the stream) and a violation returns
+ *   SATTN_ERR_INDEX; otherwise a violation is undefined behaviour (out-of-range indices are
+ *   read as zero rows, never out of bounds).
+ *   out  [B,H,Nq,D], bf16 (round to nearest even) or fp32 per out_dtype.
+ *   lse  fp32 [B,H,Nq] or NULL.
+ */
+int sattn_forward(const void* q, const void* k, const void* v,
+                  const int32_t* idx, const int32_t* counts, int cap,
+                  int B, int H, int Nq, int Nk, int D, int group, float scale,
+                  void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * attn_forward - dense control path: every query attends to every key.
+ * LongLive DiT blog, "Self Attention" and "Online Softmax": per-head softmax(Q K^T * scale) V,
+ * tiled so the score matrix is never materialised.  Same layouts, precision and lse definition
+ * as sattn_forward, with no index lists.
+ */
+int attn_forward(const void* q, const void* k, const void* v,
+                 int B, int H, int Nq, int Nk, int D, float scale,
+                 void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * sattn_voxel_permutation - host-side token order that makes every run of vt*vy*vx tokens one
+ * spatio-temporal voxel of a (T, Hg, Wg) raster grid.
+ * Chipmunk review, "What carries the argument" and Fig. 2 caption (voxel reordering so that
+ * column-sparse chunks are 3D cubes; voxel (4,6,8) in "Assumptions & free parameters").
+ * Tokens are ordered by (t/vt, y/vy, x/vx, t%vt, y%vy, x%vx).  perm is a HOST int32 array of
+ * T*Hg*Wg entries: permuted[i] = original[perm[i]].
+ */
+int sattn_voxel_permutation(int T, int Hg, int Wg, int vt, int vy, int vx, int32_t* perm);
+
+/*
+ * sattn_permute_tokens - dst[b,h,i,:] = src[b,h,perm[i],:] (inverse = 0) or
+ * dst[b,h,perm[i],:] = src[b,h,i,:] (inverse = 1) for bf16 [B,H,N,D] tensors; perm is a
+ * DEVICE int32 permutation of [0,N).  Applies and undoes the voxel order on the device.
+ */
+int sattn_permute_tokens(const void* src, void* dst, const int32_t* perm, int B, int H, int N, int D,
+                         int inverse, void* stream);
+
+const char* sattn_strerror(int status);   /* static description of a status code */
+const char* sattn_last_error(void);       /* thread-local detail of the last failed call */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SATTN_H */

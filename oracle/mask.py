@@ -44,7 +44,7 @@ def group_scores_ref(q, k, group: int, scale: float) -> np.ndarray:
     """
     qm = group_mean_ref(q, group)
     k = np.asarray(k, dtype=np.float64)
-    return np.einsum("bhgd,bhnd->bhgn", qm, k) * scale
+    return np.matmul(qm, np.swapaxes(k, -1, -2)) * scale
 
 
 def topk_select_ref(s_row: np.ndarray, topk: int) -> tuple:

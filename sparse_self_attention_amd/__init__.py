@@ -1,0 +1,198 @@
+"""Fine-grained (Mx1-slice / column-sparse) self-attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of libsattn.so (include/sattn.h).  Functions take torch
+tensors, check dtype / device / layout, and pass raw device pointers and the current HIP stream;
+all of the work runs in the library's HIP kernels.  There is no fallback: if libsattn.so is
+missing or cannot be loaded, every call raises.
+
+    idx, counts = mask(q, k, group=128, topk=k)            # or thresh=tau
+    out, lse    = forward(q, k, v, idx, counts, group=128)
+    out, lse    = attn(q, k, v)                            # dense control path
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["mask", "forward", "attn", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
+           "library_path", "SattnError", "TOPK", "THRESH"]
+
+TOPK, THRESH = 0, 1
+BF16, F32 = 0, 1
+MASK_MAX_NK = 131072
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("SATTN_LIBRARY", os.path.join(_PKG, "libsattn.so"))
+_lib = None
+
+
+class SattnError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libsattn.so not found at {_LIB_PATH}; build it with "
+                           "`python -m sparse_self_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.sattn_mask_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.sattn_mask_workspace_bytes.restype = Z
+    lib.sattn_mask.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, P, P, I, P, Z, P]
+    lib.sattn_mask.restype = I
+    lib.sattn_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, P]
+    lib.sattn_forward.restype = I
+    lib.attn_forward.argtypes = [P, P, P, I, I, I, I, I, F, P, I, P, P]
+    lib.attn_forward.restype = I
+    lib.sattn_voxel_permutation.argtypes = [I, I, I, I, I, I, P]
+    lib.sattn_voxel_permutation.restype = I
+    lib.sattn_permute_tokens.argtypes = [P, P, P, I, I, I, I, I, P]
+    lib.sattn_permute_tokens.restype = I
+    lib.sattn_strerror.argtypes = [I]
+    lib.sattn_strerror.restype = ctypes.c_char_p
+    lib.sattn_last_error.argtypes = []
+    lib.sattn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = _load()
+        raise SattnError(fn, status, lib.sattn_last_error().decode(errors="replace"))
+
+
+def _stream_ptr(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _check_qkv(q, k, v=None):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, D] tensor")
+    B, H, Nq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q and k disagree on B, H or D")
+    if v is not None and v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    return B, H, Nq, k.shape[2], D
+
+
+def mask_workspace_bytes(B: int, H: int, Nq: int, Nk: int, D: int, group: int) -> int:
+    return int(_load().sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group))
+
+
+def mask(q: torch.Tensor, k: torch.Tensor, group: int, *, topk: Optional[int] = None,
+         thresh: Optional[float] = None, scale: Optional[float] = None, cap: Optional[int] = None,
+         idx: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None):
+    """Per-group key lists from the group-mean query (sattn_mask).  Exactly one of topk / thresh."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k)
+    if (topk is None) == (thresh is None):
+        raise ValueError("pass exactly one of topk= or thresh=")
+    mode = TOPK if topk is not None else THRESH
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    G = -(-Nq // group)
+    if cap is None:
+        cap = int(topk) if mode == TOPK else Nk
+    if idx is None:
+        idx = torch.empty((B, H, G, cap), dtype=torch.int32, device=q.device)
+    if counts is None:
+        counts = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    need = lib.sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.sattn_mask(_ptr(q), _ptr(k), B, H, Nq, Nk, D, group, mode, int(topk or 0),
+                        float(thresh or 0.0), scale, _ptr(idx), _ptr(counts), idx.shape[-1],
+                        _ptr(workspace), workspace.numel(), _stream_ptr(q))
+    _check("sattn_mask", st)
+    return idx, counts
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, counts: torch.Tensor,
+            group: int, *, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16, want_lse: bool = True):
+    """Sparse attention over per-group key lists (sattn_forward).  Returns (out, lse or None)."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k, v)
+    G = -(-Nq // group)
+    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
+        raise ValueError("idx and counts must be contiguous int32")
+    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
+        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or fp32 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = lib.sattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk, D,
+                           group, scale, _ptr(out), F32 if out.dtype == torch.float32 else BF16, _ptr(lse),
+                           _stream_ptr(q))
+    _check("sattn_forward", st)
+    return out, lse
+
+
+def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+         out_dtype: torch.dtype = torch.bfloat16, want_lse: bool = True):
+    """Dense attention control path (attn_forward).  Returns (out, lse or None)."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = lib.attn_forward(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, D, scale, _ptr(out),
+                          F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
+    _check("attn_forward", st)
+    return out, lse
+
+
+def voxel_permutation(grid, voxel) -> torch.Tensor:
+    """Host int32 permutation that makes every run of prod(voxel) tokens one voxel (sattn_voxel_permutation)."""
+    lib = _load()
+    T, Hg, Wg = grid
+    perm = torch.empty(T * Hg * Wg, dtype=torch.int32)
+    _check("sattn_voxel_permutation", lib.sattn_voxel_permutation(T, Hg, Wg, *voxel, _ptr(perm)))
+    return perm
+
+
+def permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reorder the tokens of a bf16 [B,H,N,D] device tensor by a device int32 permutation."""
+    lib = _load()
+    B, H, N, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    if perm.dtype != torch.int32 or not perm.is_cuda or perm.numel() != N:
+        raise ValueError("perm must be a device int32 tensor of N entries")
+    _check("sattn_permute_tokens", lib.sattn_permute_tokens(_ptr(x), _ptr(out), _ptr(perm), B, H, N, D,
+                                                            1 if inverse else 0, _stream_ptr(x)))
+    return out

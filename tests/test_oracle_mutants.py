@@ -56,8 +56,10 @@ FWD_MUTANTS = [
 MASK_MUTANTS = [
     ("tail mean divides by M", "out[:, :, g] = q[:, :, r0:r1].sum(axis=2) / (r1 - r0)",
      "out[:, :, g] = q[:, :, r0:r1].sum(axis=2) / group"),
-    ("score scale dropped", 'return np.einsum("bhgd,bhnd->bhgn", qm, k) * scale',
-     'return np.einsum("bhgd,bhnd->bhgn", qm, k)'),
+    ("score scale dropped", "return np.matmul(qm, np.swapaxes(k, -1, -2)) * scale",
+     "return np.matmul(qm, np.swapaxes(k, -1, -2))"),
+    ("keys transposed with groups", "return np.matmul(qm, np.swapaxes(k, -1, -2)) * scale",
+     "return np.swapaxes(np.matmul(k, np.swapaxes(qm, -1, -2)), -1, -2)[..., ::-1] * scale"),
     ("top-k ties to the higher index", "np.lexsort((np.arange(n), -s_row))", "np.lexsort((-np.arange(n), -s_row))"),
     ("top-k keeps one too few", "kept = order[:topk]", "kept = order[:max(topk - 1, 1)]"),
     ("top-k keeps the lowest scores", "np.lexsort((np.arange(n), -s_row))", "np.lexsort((np.arange(n), s_row))"),
