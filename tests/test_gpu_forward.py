@@ -63,7 +63,7 @@ def test_random_lists(sattn, D, group, Nq, Nk, q_std):
     kb, vb = _rand_bits(rng, (B, H, Nk, D)), _rand_bits(rng, (B, H, Nk, D))
     G = -(-Nq // group)
     cap = min(Nk, 700)
-    special = [0, 1, 63, 64, 65, cap, min(cap, 129)]
+    special = [min(c, cap) for c in (0, 1, 63, 64, 65, cap, 129)]
     counts = rng.integers(1, cap + 1, size=(B, H, G)).astype(np.int32)
     for i, c in enumerate(special[:counts.size]):
         counts.flat[i] = c
