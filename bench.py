@@ -1,0 +1,219 @@
+"""Benchmark of the fine-grained sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path over the long-video workload (70,200 tokens on a 30x45x52
+latent grid, 24 heads of dimension 128, groups of M = 128 queries, 20 % of keys per group):
+the mean-query top-k mask (recomputed every 4th step and reused in between, with Q and K drifting
+by 5 % noise per step) plus the sparse forward over the kept keys.
+
+Prints one JSON line.  `value` is kept-FLOP throughput of the whole job (mask time included);
+the line also carries the forward-only and dense-equivalent rates, the dense control path, the
+roofline of the dominant kernel and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload long_70200] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse attn TFLOP/s (kept + dense-equiv) and % MFMA peak at 20% density, 1 GPU"
+PEAK_BF16_TFLOPS = 256 * 4 * 1024 * 2.4e9 / 1e12      # 2516.6: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz
+HBM_PEAK_GBPS = 8000.0
+MASK_EVERY = 4
+DRIFT = 0.05
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=8)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="long_70200")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-units", type=int, default=0, help="oracle units to time (default: 4 per core)")
+    p.add_argument("--kernel-only", action="store_true",
+                   help="only the timed steps (for profiler runs): no dense path, no CPU baseline")
+    return p.parse_args()
+
+
+def kept_flops(counts, w) -> float:
+    """4 D sum_{b,h,g} |g| c_g: QK^T and PV multiply-adds over the kept (query, key) pairs."""
+    import numpy as np
+    G = w.groups
+    sizes = np.full(G, w.group, dtype=np.float64)
+    sizes[-1] = w.n_q - (G - 1) * w.group
+    return float(4.0 * w.dim * (counts.astype(np.float64) * sizes[None, None, :]).sum())
+
+
+def cpu_baseline(w, qb, kb, vb, idx_h, cnt_h, n_units):
+    """Time the fp64 oracle on a seeded sample of (head, group) units in one process per core."""
+    import multiprocessing as mp
+    import numpy as np
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    if n_units <= 0:
+        n_units = 4 * cores
+    rng = np.random.default_rng(1234)
+    units = [(int(rng.integers(w.heads)), int(rng.integers(w.groups))) for _ in range(n_units - 1)]
+    units.append((w.heads - 1, w.groups - 1))                 # always include the partial tail group
+    jobs = []
+    for h, g in units:
+        r0, r1 = g * w.group, min((g + 1) * w.group, w.n_q)
+        c = int(cnt_h[0, h, g])
+        jobs.append((qb[0, h, r0:r1], kb[0, h], vb[0, h], idx_h[0, h, g, :c], w.group))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_unit, jobs[:cores])                  # warm the workers (imports)
+        t0 = time.perf_counter()
+        pool.map(_oracle_unit, jobs)
+        dt = time.perf_counter() - t0
+    sizes = [min((g + 1) * w.group, w.n_q) - g * w.group for _, g in units]
+    flops = sum(4.0 * w.dim * s * len(j[3]) for s, j in zip(sizes, jobs))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(units)} (head, group) units of the step-0 mask, fp64 masked-dense oracle, "
+                      f"one process per core, {dt:.1f} s wall"}
+
+
+def _oracle_unit(job):
+    import numpy as np
+    from oracle import sparse_attention_ref
+    from synth.inputs import bf16_bits_to_f32
+    qg, kh, vh, lst, group = job
+    q = bf16_bits_to_f32(qg)[None, None].astype(np.float64)
+    k = bf16_bits_to_f32(kh)[None, None].astype(np.float64)
+    v = bf16_bits_to_f32(vh)[None, None].astype(np.float64)
+    idx = np.asarray(lst, dtype=np.int32)[None, None, None]
+    cnt = np.array([[[len(lst)]]], dtype=np.int32)
+    out, lse = sparse_attention_ref(q, k, v, idx, cnt, group, 1.0 / math.sqrt(q.shape[-1]))
+    return float(out[0, 0, 0, 0])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import sparse_self_attention_amd as sattn
+    from synth import inputs
+
+    if not os.path.exists(sattn.library_path()):
+        from sparse_self_attention_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    qb, kb, vb = inputs.generate(w)
+    t_gen = time.perf_counter() - t_gen
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q0, k0, v = up(qb), up(kb), up(vb)
+    G, cap = w.groups, w.topk
+    steps, warm = args.steps, args.warmup
+    total = steps + warm
+    # per-step inputs: Q_s = Q_{s-1} + 0.05 rms(Q_0) N(0,1), likewise K; V fixed (made before timing)
+    gen = torch.Generator(device=dev)
+    qs, ks = [q0], [k0]
+    rq, rk = q0.float().pow(2).mean().sqrt().item(), k0.float().pow(2).mean().sqrt().item()
+    for s in range(1, total):
+        gen.manual_seed(1000 * 3 + s)
+        qs.append((qs[-1].float() + DRIFT * rq * torch.randn(q0.shape, device=dev, generator=gen)).to(torch.bfloat16))
+        ks.append((ks[-1].float() + DRIFT * rk * torch.randn(k0.shape, device=dev, generator=gen)).to(torch.bfloat16))
+    idx = torch.empty((1, w.heads, G, cap), dtype=torch.int32, device=dev)
+    counts = torch.empty((1, w.heads, G), dtype=torch.int32, device=dev)
+    ws = torch.empty(sattn.mask_workspace_bytes(1, w.heads, w.n_q, w.n_k, w.dim, w.group), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(q0)
+    lse = torch.empty((1, w.heads, w.n_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_steps(n, offset, ev=None):
+        for s in range(n):
+            i = offset + s
+            if s % MASK_EVERY == 0:
+                if ev is not None:
+                    ev["m0"][s // MASK_EVERY].record(stream)
+                sattn.mask(qs[i], ks[i], w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
+                if ev is not None:
+                    ev["m1"][s // MASK_EVERY].record(stream)
+            if ev is not None:
+                ev["f0"][s].record(stream)
+            sattn.forward(qs[i], ks[i], v, idx, counts, w.group, out=out, lse=lse)
+            if ev is not None:
+                ev["f1"][s].record(stream)
+
+    run_steps(warm, 0)
+    torch.cuda.synchronize()
+    nm = (steps + MASK_EVERY - 1) // MASK_EVERY
+    E = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ev = {"m0": E(nm), "m1": E(nm), "f0": E(steps), "f1": E(steps)}
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    run_steps(steps, warm, ev)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    fwd_ms = [a.elapsed_time(b) for a, b in zip(ev["f0"], ev["f1"])]
+    mask_ms = [a.elapsed_time(b) for a, b in zip(ev["m0"], ev["m1"])]
+    cnt_h = counts.cpu().numpy()
+    kflops = kept_flops(cnt_h, w)
+    dflops = 4.0 * w.dim * w.heads * w.n_q * w.n_k * w.batch
+    fwd_avg = float(np.mean(fwd_ms))
+    value = kflops * steps / (total_ms * 1e-3) / 1e12
+    fwd_tflops = kflops / (fwd_avg * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(total_ms / steps, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.n_q, "head_dim": w.dim,
+                   "group": w.group, "topk": w.topk, "density": round(float(cnt_h.sum()) / (cnt_h.size * w.n_k), 4),
+                   "mask_every": MASK_EVERY, "grid": list(w.grid_k)},
+        "kept_tflops_fwd": round(fwd_tflops, 2),
+        "dense_equiv_tflops_fwd": round(dflops / (fwd_avg * 1e-3) / 1e12, 2),
+        "pct_mfma_peak_kept_fwd": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_mfma_peak_kept_job": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": {"mean": round(fwd_avg, 3), "min": round(min(fwd_ms), 3), "max": round(max(fwd_ms), 3)},
+        "mask_ms": {"mean": round(float(np.mean(mask_ms)), 3), "n": len(mask_ms)},
+        "gathered_GBps_fwd": round(float(cnt_h.sum()) * 2 * w.dim * 2 / (fwd_avg * 1e-3) / 1e9, 1),
+    }
+    # dominant kernel: the sparse forward (one launch per step)
+    rec["roofline"] = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,4,sparse,bf16>",
+                       "achieved": round(fwd_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                       "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    if not args.kernel_only:
+        # dense control path on the step-0 inputs
+        dmss = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sattn.attn(q0, k0, v, out=out, lse=lse)
+            b.record(stream)
+            torch.cuda.synchronize()
+            dmss.append(a.elapsed_time(b))
+        dense_ms = float(np.median(dmss))
+        rec["dense_ms"] = round(dense_ms, 3)
+        rec["dense_tflops"] = round(dflops / (dense_ms * 1e-3) / 1e12, 2)
+        rec["speedup_vs_dense_fwd"] = round(dense_ms / fwd_avg, 3)
+        rec["speedup_vs_dense_job"] = round(dense_ms / (total_ms / steps), 3)
+    if not args.no_cpu_baseline and not args.kernel_only:
+        # oracle on the step-0 inputs with the step-0 lists
+        sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
+        torch.cuda.synchronize()
+        rec["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, idx.cpu().numpy(), counts.cpu().numpy(), args.cpu_units)
+    rec["input_gen_s"] = round(t_gen, 1)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

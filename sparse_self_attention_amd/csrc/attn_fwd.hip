@@ -52,7 +52,7 @@ struct FwdLayout {
 };
 
 template <int D, int NW, bool DENSE, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap,
     int Nq, int Nk, int group, int G, float scale_log2, void* __restrict__ out, float* __restrict__ lse,
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     bmax = pair_max(bmax) * scale_log2;
     if (__builtin_amdgcn_ballot_w64(bmax > m_run + LAZY_RESCALE_LOG2) != 0) {
       const float mnew = fmaxf(m_run, bmax);
-      const float alpha = (mnew == m_run) ? 1.0f : exp2f(m_run - mnew);
+      const float alpha = (mnew == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
       l_run *= alpha;
 #pragma unroll
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2f(__builtin_fmaf(s[kb][r], scale_log2, -m_run));
-        const float p1 = exp2f(__builtin_fmaf(s[kb][r + 1], scale_log2, -m_run));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], scale_log2, -m_run));
         pk[kb][r >> 1] = pack_bf16x2(p0, p1);
         l_run = add_bf16x2(pk[kb][r >> 1], l_run);
       }
