@@ -10,15 +10,12 @@
 //  k_scores       s[g, j] = scale * (hi_g . k_j + lo_g . k_j) with v_mfma_f32_32x32x16_bf16, in tiles
 //                 of 32 groups x 32 keys so every K row read feeds 32 groups; fp32 scores of a bounded
 //                 number of heads are staged in the workspace (sized to stay in the 256 MB MALL).
-//  k_select       one 1024-thread workgroup per group; the group's scores stay in VGPRs when there are
-//                 at most 16 per thread, else every pass re-reads them from the L2/MALL-resident stage;
-//                 - top-k: finds the k-th largest score by a 3-pass MSB-first radix select
-//                   (12 + 12 + 8 bits of an order-preserving integer key) with LDS histograms;
-//                   ties at the cut go to the lowest key index;
-//                 - threshold: lse by block max + block sum of exp, cut = lse + ln(tau); if nothing
-//                   passes, the arg-max key (lowest index on ties) is kept;
-//                 then compacts the kept keys into an ascending list: wave ballots + mbcnt give
-//                 the in-wave prefix, one block scan over the per-wave counts gives the offsets.
+//  k_select       one 1024-thread workgroup per group: top-k by an MSB-first radix select whose first
+//                 12-bit digit is histogrammed over the staged scores and whose lower 20 bits are
+//                 resolved on the keys of the cut bin copied to LDS (ties at the cut go to the lowest
+//                 key index); threshold by block max + block sum of exp, cut = lse + ln(tau), the
+//                 arg-max key if nothing passes.  Keep flags live in LDS bitmaps written by wave
+//                 ballots; the ascending list is written from popcounts, one block scan and mbcnt.
 #include <math.h>
 
 #include "../../include/sattn.h"
@@ -27,7 +24,7 @@
 
 namespace sattn {
 
-constexpr size_t SCORE_STAGE_BUDGET = 320ull << 20;   // bytes of fp32 scores staged per pass
+constexpr size_t SCORE_STAGE_BUDGET = 200ull << 20;   // bytes of fp32 scores staged per pass (MALL-sized)
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 
@@ -92,8 +89,11 @@ __global__ __launch_bounds__(256) void k_group_mean(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------------------------
 // scores: one wave = 32 groups x (KT x 32) keys
 // ---------------------------------------------------------------------------------------------
-constexpr int SC_KT = 4;   // 32-key tiles per wave
+constexpr int SC_KT = 8;   // 32-key tiles per wave
 
+// S = q_avg K^T: A = the 32 group means (rows = groups), B = K^T (columns = keys).  In the
+// accumulator layout lane l holds key j0 + l%32 for 16 groups, so each store instruction writes
+// two contiguous 128-byte runs of score rows.
 template <int D>
 __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, const uint16_t* __restrict__ qhi,
                                                  const uint16_t* __restrict__ qlo, int Nk, int G, float scale,
@@ -107,44 +107,40 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, 
   const int gt = t % gtiles;
   const int hh = t / gtiles;               // head inside this pass
   const size_t bh = (size_t)bh0 + hh;
-  const int g = gt * 32 + ql;
 
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(qhi + bh * G * D, (uint32_t)G * RB);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(qlo + bh * G * D, (uint32_t)G * RB);
-  const uint32_t goff = (uint32_t)(g < G ? g : G) * RB;   // g >= G reads zeros
-  bf16x8 bhi[KSTEPS], blo[KSTEPS];
+  const int gl = gt * 32 + ql;
+  const uint32_t goff = (uint32_t)(gl < G ? gl : G) * RB;   // g >= G reads zeros
+  bf16x8 ahi[KSTEPS], alo[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    bhi[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rh, goff + (2 * ks + hi) * 16));
-    blo[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rl, goff + (2 * ks + hi) * 16));
+    ahi[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rh, goff + (2 * ks + hi) * 16));
+    alo[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rl, goff + (2 * ks + hi) * 16));
   }
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * Nk * D, (uint32_t)Nk * RB);
-  float* srow = scores + ((size_t)hh * G + (g < G ? g : 0)) * score_stride(Nk);
+  const int stride = score_stride(Nk);
+  float* sbase = scores + (size_t)hh * G * stride;
   for (int kt = 0; kt < SC_KT; ++kt) {
     const int j0 = ((kc * 4 + wave) * SC_KT + kt) * 32;
     if (j0 >= Nk) break;
     const uint32_t koff = (uint32_t)(j0 + ql) * RB;
-    bf16x8 a[KSTEPS];
+    bf16x8 b[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      a[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rk, koff + (2 * ks + hi) * 16));
+      b[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rk, koff + (2 * ks + hi) * 16));
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bhi[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], blo[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], b[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], b[ks], acc, 0, 0, 0);
     }
-    if (g < G) {
+    const int j = j0 + ql;
+    if (j < Nk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + 8 * i + 4 * hi;
-        if (j + 3 < Nk) {
-          *(f32x4*)(srow + j) = f32x4{acc[4 * i] * scale, acc[4 * i + 1] * scale, acc[4 * i + 2] * scale,
-                                      acc[4 * i + 3] * scale};
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (j + e < Nk) srow[j + e] = acc[4 * i + e] * scale;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int g = gt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (g < G) sbase[(size_t)g * stride + j] = acc[r] * scale;
       }
     }
   }
@@ -215,135 +211,251 @@ __device__ inline int block_min_int(int x, int* red) {
   return r;
 }
 
-// Keys of the group's scores: held in VGPRs when NPT > 0 (NPT = keys per thread), otherwise
-// re-read from the staged fp32 scores (L2 / MALL resident) in every pass.  Key 0 marks "no key".
-template <int NPT>
-struct ScoreKeys {
-  static constexpr bool IN_REGS = NPT > 0;
-  uint32_t u[IN_REGS ? NPT : 1];
-  const float* srow;
-  int Nk, n;
-  __device__ void init(const float* row, int nk) {
-    srow = row;
-    Nk = nk;
-    n = IN_REGS ? NPT : (nk + SEL_THREADS - 1) / SEL_THREADS;
-    if (IN_REGS) {
-#pragma unroll
-      for (int i = 0; i < (IN_REGS ? NPT : 1); ++i) {
-        const int j = i * SEL_THREADS + (int)threadIdx.x;
-        u[i] = j < Nk ? order_key(srow[j]) : 0u;
-      }
-    }
-  }
-  __device__ uint32_t get(int i) const {
-    if (IN_REGS) return u[i];
-    const int j = i * SEL_THREADS + (int)threadIdx.x;
-    return j < Nk ? order_key(srow[j]) : 0u;
-  }
-};
-
 __device__ inline float key_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-template <int NPT>
-__global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict__ scores, int Nk, int G, int mode,
-                                                        int topk, float log_tau, int32_t* __restrict__ idx,
+// Order-preserving key of the score of key j in this group (0 = no key: j >= Nk).
+__device__ inline uint32_t key_at(const float* srow, int j, int Nk) { return j < Nk ? order_key(srow[j]) : 0u; }
+
+constexpr int SEL_CAND = 4096;                                   // LDS candidates of the cut bin
+constexpr int SEL_UNROLL = 32;                                   // loads in flight per thread
+
+// In (digit-)bin search over hist[0..nb): the bin holding the kk-th largest element, counting from
+// the top.  Thread t owns bins nb-1-per*t ... (descending); writes found[0] = bin, found[1] = rank
+// inside the bin.  Call with every thread of the block.
+__device__ inline void find_bin(const int* hist, int nb, int kk, int* wsum, int* found) {
+  const int tid = threadIdx.x;
+  const int per = nb / SEL_THREADS > 0 ? nb / SEL_THREADS : 1;
+  const bool owner = tid * per < nb;
+  int local = 0;
+  if (owner)
+    for (int e = 0; e < per; ++e) local += hist[nb - 1 - (tid * per + e)];
+  int total;
+  int above = block_excl_scan(local, wsum, total);
+  if (owner && above < kk && kk <= above + local) {
+    for (int e = 0; e < per; ++e) {
+      const int b = nb - 1 - (tid * per + e);
+      if (above < kk && kk <= above + hist[b]) {
+        found[0] = b;
+        found[1] = kk - above;
+      }
+      above += hist[b];
+    }
+  }
+  __syncthreads();
+}
+
+// One 1024-thread workgroup per group.  Keys j are visited as rows i of 1024: j = 1024 i + tid, so a
+// wave covers 64 consecutive keys of a row and its ballot is one 64-bit word pair of a bitmap.
+//  top-k:     pass 1 (global) 12-bit histogram of the top digit; pass 2 (global) marks keys above the
+//             cut bin in `strict` and copies the cut bin's keys to LDS; the lower 20 bits are resolved
+//             on those candidates (12 + 8 bit digits); candidates above the cut join `strict`, ties
+//             at the cut go to `tie`.  If the cut bin overflows the LDS list, passes 2-3 and the
+//             flags are computed from global memory instead.
+//  threshold: pass 1 max, pass 2 sum of exp, pass 3 marks s >= lse + ln tau in `strict`.
+//  Compaction: popcounts of the bitmap words per (row, wave), one block scan, then each kept key
+//  writes its index at its rank; ties are taken lowest index first up to `need`.
+static inline size_t select_lds_bytes(int Nk, bool topk) {
+  const size_t rows = (size_t)(Nk + SEL_THREADS - 1) / SEL_THREADS;
+  const size_t words = rows * (SEL_THREADS / 32);
+  return 4 * ((topk ? 4096 : 0) + 2 * words + 2 * rows * SEL_WAVES + (topk ? 2 * SEL_CAND : 0));
+}
+
+template <bool TOPK>
+__global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict__ scores, int Nk, int G, int topk,
+                                                        float log_tau, int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ counts, int cap, int bh0) {
-  constexpr int MAXROWS = NPT > 0 ? NPT : SATTN_MASK_MAX_NK / SEL_THREADS;
-  __shared__ int hist[4096];
-  __shared__ int cnt_s[MAXROWS * SEL_WAVES];
-  __shared__ int cnt_t[MAXROWS * SEL_WAVES];
+  extern __shared__ __attribute__((aligned(16))) int sel_dyn[];   // sized by select_lds_bytes(Nk, TOPK)
   __shared__ int wsum[SEL_WAVES];
   __shared__ float fred[SEL_WAVES];
   __shared__ int ired[SEL_WAVES];
   __shared__ int found[2];
+  __shared__ int ncand;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = blockIdx.x / G, g = blockIdx.x % G;
   const size_t unit = ((size_t)bh0 + hh) * G + g;
-  ScoreKeys<NPT> sk;
-  sk.init(scores + ((size_t)hh * G + g) * score_stride(Nk), Nk);
-  const int rows = sk.n;
+  const float* srow = scores + ((size_t)hh * G + g) * score_stride(Nk);
+  const int rows = (Nk + SEL_THREADS - 1) / SEL_THREADS;
+  const int words = rows * (SEL_THREADS / 32);
+  int* hist = sel_dyn;                                             // 4096 bins (top-k only)
+  uint32_t* strict_bits = (uint32_t*)(sel_dyn + (TOPK ? 4096 : 0)); // words
+  uint32_t* tie_bits = strict_bits + words;                        // words
+  int* cnt_s = (int*)(tie_bits + words);                           // rows * 16
+  int* cnt_t = cnt_s + rows * SEL_WAVES;                           // rows * 16
+  uint32_t* cand_key = (uint32_t*)(cnt_t + rows * SEL_WAVES);      // SEL_CAND (top-k only)
+  int* cand_j = (int*)(cand_key + SEL_CAND);                       // SEL_CAND (top-k only)
 
-  uint32_t cut;     // keep u > cut, plus the first `need` keys with u == cut
+  for (int w = tid; w < words; w += SEL_THREADS) { strict_bits[w] = 0u; tie_bits[w] = 0u; }
+  if (tid == 0) ncand = 0;
   int need = 0;
-  if (mode == 0) {
-    uint32_t prefix = 0, pmask = 0;
-    int kk = topk;
-    const int shifts[3] = {20, 8, 0};
-    const int widths[3] = {12, 12, 8};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = shifts[pass], nb = 1 << widths[pass];
-      for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
-      if (tid == 0) { found[0] = 0; found[1] = 1; }
-      __syncthreads();
-#pragma unroll(NPT > 0 ? NPT : 1)
-      for (int i = 0; i < rows; ++i) {
-        const uint32_t u = sk.get(i);
-        if ((u & pmask) == prefix && u != 0u) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+
+  if (TOPK) {
+    for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0;
+    if (tid == 0) { found[0] = 0; found[1] = 1; }
+    __syncthreads();
+    // pass 1: top 12 bits
+    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
+      uint32_t u[SEL_UNROLL];
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e)
+        if (u[e] != 0u) atomicAdd(&hist[u[e] >> 20], 1);
+    }
+    __syncthreads();
+    find_bin(hist, 4096, topk, wsum, found);
+    const uint32_t b1 = (uint32_t)found[0];
+    int kk = found[1];
+    __syncthreads();
+    // pass 2: keys above the cut bin -> strict bits; keys in it -> LDS candidates
+    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
+      uint32_t u[SEL_UNROLL];
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) {
+        const int i = i0 + e;
+        if (i < rows) {
+          const uint64_t above = __builtin_amdgcn_ballot_w64(u[e] != 0u && (u[e] >> 20) > b1);
+          if (lane == 0) {
+            const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
+            strict_bits[w0] = (uint32_t)above;
+            strict_bits[w0 + 1] = (uint32_t)(above >> 32);
+          }
+          if (u[e] != 0u && (u[e] >> 20) == b1) {
+            const int pos = atomicAdd(&ncand, 1);
+            if (pos < SEL_CAND) { cand_key[pos] = u[e]; cand_j[pos] = i * SEL_THREADS + tid; }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int nc = ncand;
+    uint32_t prefix = b1 << 20;
+    if (nc <= SEL_CAND) {
+      // lower digits on the LDS candidates
+      const int shifts[2] = {8, 0};
+      const int widths[2] = {12, 8};
+      uint32_t pmask = 0xfff00000u;
+      for (int pass = 0; pass < 2; ++pass) {
+        const int sh = shifts[pass], nb = 1 << widths[pass];
+        for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
+        if (tid == 0) { found[0] = 0; found[1] = 1; }
+        __syncthreads();
+        for (int x = tid; x < nc; x += SEL_THREADS) {
+          const uint32_t u = cand_key[x];
+          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+        }
+        __syncthreads();
+        find_bin(hist, nb, kk, wsum, found);
+        prefix |= (uint32_t)found[0] << sh;
+        pmask |= (uint32_t)(nb - 1) << sh;
+        kk = found[1];
+        __syncthreads();
+      }
+      need = kk;
+      // candidates above the cut are kept; those equal to it are ties
+      for (int x = tid; x < nc; x += SEL_THREADS) {
+        const uint32_t u = cand_key[x];
+        const int j = cand_j[x];
+        if (u > prefix) atomicOr(&strict_bits[j >> 5], 1u << (j & 31));
+        else if (u == prefix) atomicOr(&tie_bits[j >> 5], 1u << (j & 31));
       }
       __syncthreads();
-      // thread t owns bins nb-1-per*t ... (descending); its exclusive scan = count above them
-      const int per = nb / SEL_THREADS > 0 ? nb / SEL_THREADS : 1;
-      const bool owner = tid * per < nb;
-      int local = 0;
-      if (owner)
-        for (int e = 0; e < per; ++e) local += hist[nb - 1 - (tid * per + e)];
-      int total;
-      int above = block_excl_scan(local, wsum, total);
-      if (owner && above < kk && kk <= above + local) {
-        for (int e = 0; e < per; ++e) {
-          const int b = nb - 1 - (tid * per + e);
-          if (above < kk && kk <= above + hist[b]) {
-            found[0] = b;
-            found[1] = kk - above;
-          }
-          above += hist[b];
+    } else {
+      // the cut bin is too crowded for LDS: resolve the lower digits from global memory
+      const int shifts[2] = {8, 0};
+      const int widths[2] = {12, 8};
+      uint32_t pmask = 0xfff00000u;
+      for (int pass = 0; pass < 2; ++pass) {
+        const int sh = shifts[pass], nb = 1 << widths[pass];
+        for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
+        if (tid == 0) { found[0] = 0; found[1] = 1; }
+        __syncthreads();
+        for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
+          uint32_t u[SEL_UNROLL];
+#pragma unroll
+          for (int e = 0; e < SEL_UNROLL; ++e)
+            u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+#pragma unroll
+          for (int e = 0; e < SEL_UNROLL; ++e)
+            if (u[e] != 0u && (u[e] & pmask) == prefix) atomicAdd(&hist[(u[e] >> sh) & (nb - 1)], 1);
+        }
+        __syncthreads();
+        find_bin(hist, nb, kk, wsum, found);
+        prefix |= (uint32_t)found[0] << sh;
+        pmask |= (uint32_t)(nb - 1) << sh;
+        kk = found[1];
+        __syncthreads();
+      }
+      need = kk;
+      for (int i = 0; i < rows; ++i) {
+        const uint32_t u = key_at(srow, i * SEL_THREADS + tid, Nk);
+        const uint64_t st = __builtin_amdgcn_ballot_w64(u > prefix);
+        const uint64_t ti = __builtin_amdgcn_ballot_w64(u == prefix && u != 0u);
+        if (lane == 0) {
+          const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
+          strict_bits[w0] = (uint32_t)st;
+          strict_bits[w0 + 1] = (uint32_t)(st >> 32);
+          tie_bits[w0] = (uint32_t)ti;
+          tie_bits[w0 + 1] = (uint32_t)(ti >> 32);
         }
       }
       __syncthreads();
-      prefix |= (uint32_t)found[0] << sh;
-      pmask |= (uint32_t)(nb - 1) << sh;
-      kk = found[1];
-      __syncthreads();
     }
-    cut = prefix;
-    need = kk;
   } else {
+    __syncthreads();
     float m = -INFINITY;
-#pragma unroll(NPT > 0 ? NPT : 1)
-    for (int i = 0; i < rows; ++i) {
-      const uint32_t u = sk.get(i);
-      if (u != 0u) m = fmaxf(m, key_to_float(u));
+    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
+      uint32_t u[SEL_UNROLL];
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e)
+        if (u[e] != 0u) m = fmaxf(m, key_to_float(u[e]));
     }
     m = block_max(m, fred);
-    float s = 0.0f;
-#pragma unroll(NPT > 0 ? NPT : 1)
-    for (int i = 0; i < rows; ++i) {
-      const uint32_t u = sk.get(i);
-      if (u != 0u) s += expf(key_to_float(u) - m);
+    float ssum = 0.0f;
+    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
+      uint32_t u[SEL_UNROLL];
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e)
+        if (u[e] != 0u) ssum += expf(key_to_float(u[e]) - m);
     }
-    s = block_sum(s, fred);
-    const float t = m + logf(s) + log_tau;   // log_tau = -inf keeps every key
+    ssum = block_sum(ssum, fred);
+    const float t = m + logf(ssum) + log_tau;   // log_tau = -inf keeps every key
     // keep s_j >= t  <=>  order_key(s_j) >= order_key(t), i.e. u > cut with cut = key(t) - 1
-    const uint32_t kt = (isinf(t) && t < 0.0f) ? 1u : order_key(t);
-    cut = kt - 1u;
-    need = 0;
+    const uint32_t cut = ((isinf(t) && t < 0.0f) ? 1u : order_key(t)) - 1u;
+    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
+      uint32_t u[SEL_UNROLL];
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) {
+        const int i = i0 + e;
+        if (i < rows) {
+          const uint64_t st = __builtin_amdgcn_ballot_w64(u[e] > cut);
+          if (lane == 0) {
+            const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
+            strict_bits[w0] = (uint32_t)st;
+            strict_bits[w0 + 1] = (uint32_t)(st >> 32);
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
 
-  // ---- compaction in ascending key order j = i*1024 + tid ----
-#pragma unroll(NPT > 0 ? NPT : 1)
-  for (int i = 0; i < rows; ++i) {
-    const uint32_t u = sk.get(i);
-    const uint64_t bs = __builtin_amdgcn_ballot_w64(u > cut);
-    const uint64_t bt = __builtin_amdgcn_ballot_w64(u == cut && need > 0);
-    if (lane == 0) {
-      cnt_s[i * SEL_WAVES + wave] = __popcll(bs);
-      cnt_t[i * SEL_WAVES + wave] = __popcll(bt);
-    }
+  // ---- compaction in ascending key order ----
+  for (int x = tid; x < rows * SEL_WAVES; x += SEL_THREADS) {
+    const int w0 = x * 2;   // (row, wave) entry x owns bitmap words 2x, 2x+1
+    cnt_s[x] = __popc(strict_bits[w0]) + __popc(strict_bits[w0 + 1]);
+    cnt_t[x] = __popc(tie_bits[w0]) + __popc(tie_bits[w0 + 1]);
   }
   __syncthreads();
-  // exclusive scan over the rows*16 (row, wave) entries in row-major order
   const int nent = rows * SEL_WAVES;
   const int E = (nent + SEL_THREADS - 1) / SEL_THREADS;
   int ls = 0, lt = 0;
@@ -369,17 +481,14 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
   int32_t* out = idx + unit * (size_t)cap;
   const int kept = tot_s + min(tot_t, need);
   if (kept > 0) {
-#pragma unroll(NPT > 0 ? NPT : 1)
     for (int i = 0; i < rows; ++i) {
-      const uint32_t u = sk.get(i);
-      const bool st = u > cut;
-      const bool tie = u == cut && need > 0;
-      const uint64_t bs = __builtin_amdgcn_ballot_w64(st);
-      const uint64_t bt = __builtin_amdgcn_ballot_w64(tie);
-      const int before_s = cnt_s[i * SEL_WAVES + wave] +
-                           (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u));
-      const int before_t = cnt_t[i * SEL_WAVES + wave] +
-                           (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+      const int x = i * SEL_WAVES + wave;
+      const uint64_t bs = (uint64_t)strict_bits[2 * x] | ((uint64_t)strict_bits[2 * x + 1] << 32);
+      const uint64_t bt = (uint64_t)tie_bits[2 * x] | ((uint64_t)tie_bits[2 * x + 1] << 32);
+      const bool st = (bs >> lane) & 1u;
+      const bool tie = ((bt >> lane) & 1u) && need > 0;
+      const int before_s = cnt_s[x] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u));
+      const int before_t = cnt_t[x] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
       const bool keep = st || (tie && before_t < need);
       const int pos = before_s + min(before_t, need);
       if (keep && pos < cap) out[pos] = i * SEL_THREADS + tid;
@@ -389,7 +498,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
     // threshold mode with no key at the cut: keep the arg-max, lowest index on ties
     uint32_t best = 0;
     for (int i = 0; i < rows; ++i) {
-      const uint32_t u = sk.get(i);
+      const uint32_t u = key_at(srow, i * SEL_THREADS + tid, Nk);
       best = u > best ? u : best;
     }
     for (int off = 32; off > 0; off >>= 1) {
@@ -403,7 +512,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
     __syncthreads();
     int jmin = 0x7fffffff;
     for (int i = 0; i < rows; ++i) {
-      const uint32_t u = sk.get(i);
+      const uint32_t u = key_at(srow, i * SEL_THREADS + tid, Nk);
       if (u == bmax && u != 0u) jmin = min(jmin, i * SEL_THREADS + tid);
     }
     jmin = block_min_int(jmin, ired);
@@ -431,19 +540,26 @@ static int launch_mask_d(const MaskArgs& a) {
   const int hp = mask_heads_per_pass(BH, G, a.Nk);
   const int gtiles = (G + 31) / 32;
   const int kchunks = (a.Nk + 4 * SC_KT * 32 - 1) / (4 * SC_KT * 32);
-  const int npt = (a.Nk + SEL_THREADS - 1) / SEL_THREADS;
   const float log_tau = a.mode == 1 ? (a.thresh > 0.0f ? logf(a.thresh) : -INFINITY) : 0.0f;
+  // dynamic LDS of the select kernel can exceed 64 KB (up to ~98 KB at the largest Nk)
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    const int max_lds = (int)select_lds_bytes(SATTN_MASK_MAX_NK, true);
+    err = (int)hipFuncSetAttribute((const void*)k_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (!err)
+      err = (int)hipFuncSetAttribute((const void*)k_select<false>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (err) return err;
+    lds_attr_set = true;
+  }
   for (int bh0 = 0; bh0 < BH; bh0 += hp) {
     const int n = BH - bh0 < hp ? BH - bh0 : hp;
     hipLaunchKernelGGL((k_scores<D>), dim3(n * gtiles * kchunks), dim3(256), 0, st, (const uint16_t*)a.k, qhi, qlo,
                        a.Nk, G, a.scale, scores, bh0, gtiles, kchunks);
-#define SATTN_SEL(NPT_)                                                                                   \
-  hipLaunchKernelGGL((k_select<NPT_>), dim3(n * G), dim3(SEL_THREADS), 0, st, scores, a.Nk, G, a.mode, a.topk, \
-                     log_tau, a.idx, a.counts, a.cap, bh0)
-    if (npt <= 4) SATTN_SEL(4);
-    else if (npt <= 8) SATTN_SEL(8);
-    else if (npt <= 16) SATTN_SEL(16);
-    else SATTN_SEL(0);
+#define SATTN_SEL(T_)                                                                                     \
+  hipLaunchKernelGGL((k_select<T_>), dim3(n * G), dim3(SEL_THREADS), select_lds_bytes(a.Nk, T_), st, scores,    \
+                     a.Nk, G, a.topk, log_tau, a.idx, a.counts, a.cap, bh0)
+    if (a.mode == 0) SATTN_SEL(true);
+    else SATTN_SEL(false);
 #undef SATTN_SEL
     err = (int)hipGetLastError();
     if (err) return err;

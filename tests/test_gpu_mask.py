@@ -100,3 +100,19 @@ def test_chunked_window_threshold_density(sattn):
     idx, cnt = _gpu_mask(sattn, qb[:, :2], kb[:, :2], w.group, thresh=tau)
     dens = cnt.sum() / (cnt.size * w.n_k)
     assert abs(dens - 0.3) < 0.01, dens
+
+
+def test_crowded_cut_bin_uses_global_passes(sattn):
+    """More than 8192 keys share the top 12 bits of the cut: the lower digits come from global memory."""
+    rng = np.random.default_rng(11)
+    D, group, Nq, Nk = 64, 64, 128, 40000
+    qb = _bits(rng, (1, 1, Nq, D))
+    base = rng.standard_normal(D).astype(np.float32)
+    kb = inputs.f32_to_bf16_bits(base[None, None, None, :] + 0.02 * rng.standard_normal((1, 1, Nk, D)).astype(np.float32))
+    ref = oracle.mask_ref(f64(qb), f64(kb), group, "topk", topk=9000)
+    idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=9000)
+    check_mask_sets(idx, cnt, ref, _all_units(1, 1, 2), "crowded topk", exact_counts=True)
+    # all-equal scores over more keys than the LDS candidate list holds
+    kb = np.broadcast_to(kb[:, :, :1], (1, 1, Nk, D)).copy()
+    idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=20000)
+    assert np.all(cnt == 20000) and np.all(idx == np.arange(20000))
