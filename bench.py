@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--cpu-units", type=int, default=0, help="oracle units to time (default: 4 per core)")
     p.add_argument("--kernel-only", action="store_true",
                    help="only the timed steps (for profiler runs): no dense path, no CPU baseline")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after the steps, run one plain device copy of this many MiB (a known-size kernel "
+                        "for scaling FETCH_SIZE / WRITE_SIZE counter runs)")
     return p.parse_args()
 
 
@@ -191,6 +194,13 @@ def main():
     rec["roofline"] = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,4,sparse,bf16>",
                        "achieved": round(fwd_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                        "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = src.numel() * 4
+        del src, dst
     if not args.kernel_only:
         # dense control path on the step-0 inputs
         dmss = []

@@ -28,21 +28,27 @@
 //    combination of the kept V rows with weights that sum to one.
 //  * LDS rows are XOR-swizzled in 16-byte chunks: K rows so that 16 consecutive rows read at
 //    the same chunk hit distinct banks, V rows so that the 4-row transposed reads do.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace sattn {
 
-constexpr int BK = 64;                     // kept keys per block
-constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // move the running max only when it grows by > 2^8
+// The running max is kept until a probability could reach 2^RESCALE_LOG2 (checked through the block's
+// partial row sums); fp32 and bf16 carry such values exactly, so only the first block and the rare
+// blocks that trip the check take a block max.
+constexpr float RESCALE_LOG2 = 64.0f;
 
-template <int D>
+template <int D, int BKEYS>
 struct FwdLayout {
   static constexpr int RB = D * 2;                    // bytes per K/V row
   static constexpr int NC = D / 8;                    // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 1024 / RB;     // rows filled by one 64-lane 16-byte load
-  static constexpr int ROWSETS = BK / ROWS_PER_LOAD;  // load instructions per K (or V) block
-  static constexpr int MAT_BYTES = BK * RB;
+  static constexpr int ROWSETS = BKEYS / ROWS_PER_LOAD;  // load instructions per K (or V) block
+  static constexpr int MAT_BYTES = BKEYS * RB;
   static constexpr int STAGE_BYTES = 2 * MAT_BYTES;   // K block + V block
   static constexpr int KSTEPS = D / 16;               // MFMA k-steps over the head dim
   static constexpr int DBLK = D / 32;                 // 32-wide output column blocks
@@ -51,24 +57,31 @@ struct FwdLayout {
   __device__ static inline int swz_v(int row) { return 4 * ((row / ROWDIV) % (NC / 4)); }
 };
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Lean variant: blocks of 32 kept keys, K+V double-buffered (32 KB of LDS at D = 128) and no
+// cross-block register pipeline, so three workgroups (12 waves) fit per CU and the SIMDs
+// interleave MFMA and softmax work of different waves.
+constexpr int BKL = 32;
+
 template <int D, int NW, bool DENSE, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_lean(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap,
     int Nq, int Nk, int group, int G, float scale_log2, void* __restrict__ out, float* __restrict__ lse,
     uint32_t n_units) {
-  using L = FwdLayout<D>;
-  constexpr int NRS = (L::ROWSETS + NW - 1) / NW;      // row-sets gathered by each wave
+  using L = FwdLayout<D, BKL>;
+  constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_BYTES];
 
   const uint32_t unit = xcd_contiguous(blockIdx.x, n_units);
   const int g = (int)(unit % (uint32_t)G);
   const uint32_t bh = unit / (uint32_t)G;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hi = lane >> 5;          // which half of the wave (selects k sub-range of an MFMA)
-  const int ql = lane & 31;          // the query row of this lane inside the wave's 32 rows
-
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5;
+  const int ql = lane & 31;
   const int r0 = g * group;
   const int rows_in_group = min(group, Nq - r0);
   const int wrow = wave * 32 + ql;
@@ -81,15 +94,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     c = counts[bh * (uint32_t)G + g];
     c = c < 0 ? 0 : (c > cap ? cap : c);
   }
-  const int nblk = (c + BK - 1) / BK;
-
-  const uint16_t* khead = k + (size_t)bh * Nk * D;
-  const uint16_t* vhead = v + (size_t)bh * Nk * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(khead, (uint32_t)Nk * L::RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vhead, (uint32_t)Nk * L::RB);
+  const int nblk = (c + BKL - 1) / BKL;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
   const int32_t* ilist = DENSE ? nullptr : idx + ((size_t)bh * G + g) * (size_t)cap;
 
-  // ---- the wave's 32 query rows as MFMA B operands (Q^T), zero outside the group ----
   bf16x8 qf[L::KSTEPS];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (size_t)bh * Nq * D, (uint32_t)Nq * L::RB);
@@ -98,34 +107,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ks = 0; ks < L::KSTEPS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rq, rowoff + (uint32_t)(2 * ks + hi) * 16));
   }
+  uint32_t koff[L::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < L::KSTEPS; ++ks) koff[ks] = ql * L::RB + 16 * ((2 * ks + hi) ^ L::swz_k(ql));
+  const int s16 = lane & 15, g16 = lane >> 4;
+  const int vrow = 4 * hi + (s16 >> 2);
+  uint32_t voff[L::DBLK];
+#pragma unroll
+  for (int db = 0; db < L::DBLK; ++db)
+    voff[db] = vrow * L::RB + 16 * ((4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ L::swz_v(vrow)) + 8 * (s16 & 1);
 
-  // ---- gather: each lane owns one 16-byte chunk of one row per load instruction ----
   const int row_in = lane / L::NC;
   const int pchunk = lane % L::NC;
-  int keyreg[NRS];
+  uint32_t kch[NRS], vch[NRS];
+#pragma unroll
+  for (int j = 0; j < NRS; ++j) {
+    const int row = (wave + j * NW) * L::ROWS_PER_LOAD + row_in;
+    kch[j] = 16u * (uint32_t)(pchunk ^ L::swz_k(row));
+    vch[j] = 16u * (uint32_t)(pchunk ^ L::swz_v(row));
+  }
+  int keys[NRS];
   auto fetch_keys = [&](int blk) {
 #pragma unroll
     for (int j = 0; j < NRS; ++j) {
       const int rs = wave + j * NW;
-      const int p = blk * BK + rs * L::ROWS_PER_LOAD + row_in;
-      if (DENSE) {
-        keyreg[j] = p < Nk ? p : Nk - 1;
-      } else {
-        keyreg[j] = (rs < L::ROWSETS) ? ilist[p < c ? p : c - 1] : 0;
-      }
+      const int p = blk * BKL + rs * L::ROWS_PER_LOAD + row_in;
+      if (DENSE) keys[j] = p < Nk ? p : Nk - 1;
+      else if (L::ROWSETS % NW == 0 || rs < L::ROWSETS) keys[j] = ilist[p < c ? p : c - 1];
     }
   };
-  auto issue_gather = [&](int stage) {
-    char* sk = smem + stage * L::STAGE_BYTES;
-    char* sv = sk + L::MAT_BYTES;
+  auto issue = [&](char* stage) {
 #pragma unroll
     for (int j = 0; j < NRS; ++j) {
       const int rs = wave + j * NW;
-      if (rs < L::ROWSETS) {
-        const int row = rs * L::ROWS_PER_LOAD + row_in;
-        const uint32_t base = (uint32_t)keyreg[j] * L::RB;
-        buffer_load_lds_x4(rk, sk + rs * L::ROWS_PER_LOAD * L::RB, base + 16u * (uint32_t)(pchunk ^ L::swz_k(row)));
-        buffer_load_lds_x4(rv, sv + rs * L::ROWS_PER_LOAD * L::RB, base + 16u * (uint32_t)(pchunk ^ L::swz_v(row)));
+      if (L::ROWSETS % NW == 0 || rs < L::ROWSETS) {
+        const uint32_t base = (uint32_t)keys[j] * L::RB;
+        buffer_load_lds_x4(rk, stage + rs * L::ROWS_PER_LOAD * L::RB, base + kch[j]);
+        buffer_load_lds_x4(rv, stage + L::MAT_BYTES + rs * L::ROWS_PER_LOAD * L::RB, base + vch[j]);
       }
     }
   };
@@ -133,105 +151,92 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   f32x16 o[L::DBLK];
 #pragma unroll
   for (int i = 0; i < L::DBLK; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;   // running max, in log2 units of the scaled score
-  float l_run = 0.0f;        // this lane's part of the running sum
+  float m_run = -INFINITY, l_run = 0.0f;
 
-  if (nblk > 0) {
-    fetch_keys(0);
-    issue_gather(0);
-    if (nblk > 1) fetch_keys(1);
-  }
-
-  const int s16 = lane & 15;
-  const int g16 = lane >> 4;
-
-  for (int blk = 0; blk < nblk; ++blk) {
+  auto block = [&](auto st, int j) {
+    constexpr int ST = decltype(st)::value;
     wait_vmcnt0();
     __syncthreads();
-    if (blk + 1 < nblk) {
-      issue_gather((blk + 1) & 1);
-      if (blk + 2 < nblk) fetch_keys(blk + 2);
+    if (j + 1 < nblk) {
+      issue(smem + (1 - ST) * L::STAGE_BYTES);
+      if (j + 2 < nblk) fetch_keys(j + 2);
     }
-    const char* sk = smem + (blk & 1) * L::STAGE_BYTES;
+    const char* sk = smem + ST * L::STAGE_BYTES;
     const char* sv = sk + L::MAT_BYTES;
-
-    // ---- S^T = K Q^T for two 32-key sub-blocks ----
-    f32x16 s[2];
+    f32x16 sacc = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + ql;
-      const char* rowp = sk + row * L::RB;
-      const int sw = L::swz_k(row);
-#pragma unroll
-      for (int ks = 0; ks < L::KSTEPS; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(rowp + 16 * ((2 * ks + hi) ^ sw));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
+    for (int ks = 0; ks < L::KSTEPS; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(sk + koff[ks]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
     }
-
-    // ---- mask the unfilled tail of the last block ----
-    if (blk == nblk - 1 && (c & (BK - 1))) {
-      const int valid = c - blk * BK;
+    if (j == nblk - 1 && (c & (BKL - 1))) {
+      const int valid = c - j * BKL;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= valid) s[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hi + (r & 3) >= valid) sacc[r] = -INFINITY;
     }
-
-    // ---- online softmax (base 2) ----
-    float bmax = -INFINITY;
+    // running max: taken on the first block; afterwards only when this block's probabilities could
+    // exceed 2^RESCALE_LOG2 (some lane's partial sum trips the bound, which an exp overflow also does)
+    auto take_max = [&]() {
+      float bmax = sacc[0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kb][r]);
-    bmax = pair_max(bmax) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(bmax > m_run + LAZY_RESCALE_LOG2) != 0) {
+      for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, sacc[r]);
+      bmax = pair_max(bmax) * scale_log2;
       const float mnew = fmaxf(m_run, bmax);
       const float alpha = (mnew == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < L::DBLK; ++i) o[i] *= alpha;
-    }
-    uint32_t pk[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    };
+    uint32_t pk[8];
+    float lsum;
+    auto exps = [&]() {
+      lsum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], scale_log2, -m_run));
-        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-        l_run = add_bf16x2(pk[kb][r >> 1], l_run);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r + 1], scale_log2, -m_run));
+        pk[r >> 1] = pack_bf16x2(p0, p1);
+        lsum = add_bf16x2(pk[r >> 1], lsum);
       }
+    };
+    if (j == 0) take_max();
+    exps();
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= 0x1p64f)) != 0) {   // also true for inf / nan
+      take_max();
+      exps();
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const u32x4 bw = {pk[4 * tt], pk[4 * tt + 1], pk[4 * tt + 2], pk[4 * tt + 3]};
+#pragma unroll
+      for (int db = 0; db < L::DBLK; ++db) {
+        const char* p0 = sv + (tt * 16) * L::RB + voff[db];
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SATTN_LDS_PTR(i16x4, p0));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SATTN_LDS_PTR(i16x4, p0 + 8 * L::RB));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
+        const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), __builtin_bit_cast(bf16x8, bw),
+                                                       o[db], 0, 0, 0);
+      }
+    }
+  };
 
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 bw = {pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]};
-        const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-        const int row0 = kb * 32 + t * 16 + 4 * hi + (s16 >> 2);
-        const int row1 = row0 + 8;
-#pragma unroll
-        for (int db = 0; db < L::DBLK; ++db) {
-          const int chunk = 4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1);
-          const int within = 8 * (s16 & 1);
-          const char* p0 = sv + row0 * L::RB + 16 * (chunk ^ L::swz_v(row0)) + within;
-          const char* p1 = sv + row1 * L::RB + 16 * (chunk ^ L::swz_v(row1)) + within;
-          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SATTN_LDS_PTR(i16x4, p0));
-          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SATTN_LDS_PTR(i16x4, p1));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
-          const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
-          const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), b, o[db], 0, 0, 0);
-        }
-      }
+  if (nblk > 0) {
+    fetch_keys(0);
+    issue(smem);
+    if (nblk > 1) fetch_keys(1);
   }
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    block(IC<0>{}, j);
+    block(IC<1>{}, j + 1);
+  }
+  if (j < nblk) block(IC<0>{}, j);
 
-  // ---- epilogue: out = O / l, lse = m ln2 + ln l ----
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_valid) {
@@ -243,11 +248,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int d0 = 32 * db + 8 * i + 4 * hi;
         const float x0 = o[db][4 * i] * inv, x1 = o[db][4 * i + 1] * inv;
         const float x2 = o[db][4 * i + 2] * inv, x3 = o[db][4 * i + 3] * inv;
-        if (OUT_F32) {
-          *(f32x4*)((float*)out + orow + d0) = f32x4{x0, x1, x2, x3};
-        } else {
-          *(u32x2*)((uint16_t*)out + orow + d0) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-        }
+        if (OUT_F32) *(f32x4*)((float*)out + orow + d0) = f32x4{x0, x1, x2, x3};
+        else *(u32x2*)((uint16_t*)out + orow + d0) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
       }
     if (lse != nullptr && hi == 0)
       lse[(size_t)bh * Nq + r0 + wrow] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
@@ -255,17 +257,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 template <int D, int NW, bool DENSE>
-static int launch_fwd_t(const FwdArgs& a) {
+static int launch_lean_t(const FwdArgs& a) {
   const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
   const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)a.stream;
   if (a.out_f32)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, DENSE, true>), dim3(n_units), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, DENSE, false>), dim3(n_units), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
   return (int)hipGetLastError();
@@ -273,12 +275,12 @@ static int launch_fwd_t(const FwdArgs& a) {
 
 template <int D>
 static int launch_fwd_d(const FwdArgs& a) {
-  if (a.dense) return launch_fwd_t<D, 4, true>(a);
+  if (a.dense) return launch_lean_t<D, 4, true>(a);
   const int waves = (a.group + 31) / 32;
-  if (waves <= 2) return launch_fwd_t<D, 2, false>(a);
-  if (waves <= 4) return launch_fwd_t<D, 4, false>(a);
-  if (waves <= 6) return launch_fwd_t<D, 6, false>(a);
-  return launch_fwd_t<D, 8, false>(a);
+  if (waves <= 2) return launch_lean_t<D, 2, false>(a);
+  if (waves <= 4) return launch_lean_t<D, 4, false>(a);
+  if (waves <= 6) return launch_lean_t<D, 6, false>(a);
+  return launch_lean_t<D, 8, false>(a);
 }
 
 int launch_attn_fwd(const FwdArgs& a) {
