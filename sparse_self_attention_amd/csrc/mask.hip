@@ -8,14 +8,17 @@
 //                 stored as an unevaluated bf16 pair hi + lo (hi = bf16(mean), lo = bf16(mean - hi)),
 //                 so the matrix cores score with about 16 mantissa bits of the mean.
 //  k_scores       s[g, j] = scale * (hi_g . k_j + lo_g . k_j) with v_mfma_f32_32x32x16_bf16, in tiles
-//                 of 32 groups x 32 keys so every K row read feeds 32 groups; fp32 scores of a bounded
+//                 of 128 groups x 32 keys so every K row read feeds 128 groups; fp32 scores of a bounded
 //                 number of heads are staged in the workspace (sized to stay in the 256 MB MALL).
-//  k_select       one 1024-thread workgroup per group: top-k by an MSB-first radix select whose first
-//                 12-bit digit is histogrammed over the staged scores and whose lower 20 bits are
-//                 resolved on the keys of the cut bin copied to LDS (ties at the cut go to the lowest
-//                 key index); threshold by block max + block sum of exp, cut = lse + ln(tau), the
-//                 arg-max key if nothing passes.  Keep flags live in LDS bitmaps written by wave
-//                 ballots; the ascending list is written from popcounts, one block scan and mbcnt.
+//  k_select       one 1024-thread workgroup per group.  Top-k: a histogram of a hashed sample of
+//                 4096 scores locates the cut to within ~3.5 sigma of sampling error; one pass over the
+//                 staged scores marks the keys above that band and copies the keys inside it to LDS,
+//                 where a 12 + 12 + 8 bit radix select finds the exact k-th largest (ties go to the
+//                 lowest key index).  If the band misses the cut or overflows LDS, the cut is found
+//                 by radix passes over the staged scores instead.  Threshold: block max + block sum
+//                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Keep flags live in
+//                 LDS bitmaps written by wave ballots; the ascending list is written from popcounts,
+//                 one block scan and mbcnt.
 #include <math.h>
 
 #include "../../include/sattn.h"
@@ -89,11 +92,12 @@ __global__ __launch_bounds__(256) void k_group_mean(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------------------------
 // scores: one wave = 32 groups x (KT x 32) keys
 // ---------------------------------------------------------------------------------------------
-constexpr int SC_KT = 8;   // 32-key tiles per wave
+constexpr int SC_KT = 8;   // 32-key tiles per workgroup
 
-// S = q_avg K^T: A = the 32 group means (rows = groups), B = K^T (columns = keys).  In the
-// accumulator layout lane l holds key j0 + l%32 for 16 groups, so each store instruction writes
-// two contiguous 128-byte runs of score rows.
+// S = q_avg K^T: A = 32 group means (rows = groups), B = K^T (columns = keys).  The 4 waves of a
+// workgroup own 4 different 32-group tiles and walk the same SC_KT x 32 keys, so each K row is
+// fetched once per workgroup.  In the accumulator layout lane l holds key j0 + l%32 for 16 groups:
+// each store instruction writes two contiguous 128-byte runs of score rows.
 template <int D>
 __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, const uint16_t* __restrict__ qhi,
                                                  const uint16_t* __restrict__ qlo, int Nk, int G, float scale,
@@ -104,9 +108,11 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, 
   const int hi = lane >> 5, ql = lane & 31;
   int t = blockIdx.x;
   const int kc = t % kchunks; t /= kchunks;
-  const int gt = t % gtiles;
+  const int gq = t % gtiles;               // quad of 32-group tiles
   const int hh = t / gtiles;               // head inside this pass
   const size_t bh = (size_t)bh0 + hh;
+  const int gt = gq * 4 + wave;            // this wave's 32-group tile
+  if (gt * 32 >= G) return;                // no barrier below: a wave may leave early
 
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(qhi + bh * G * D, (uint32_t)G * RB);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(qlo + bh * G * D, (uint32_t)G * RB);
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, 
   const int stride = score_stride(Nk);
   float* sbase = scores + (size_t)hh * G * stride;
   for (int kt = 0; kt < SC_KT; ++kt) {
-    const int j0 = ((kc * 4 + wave) * SC_KT + kt) * 32;
+    const int j0 = (kc * SC_KT + kt) * 32;
     if (j0 >= Nk) break;
     const uint32_t koff = (uint32_t)(j0 + ql) * RB;
     bf16x8 b[KSTEPS];
@@ -218,7 +224,8 @@ __device__ inline float key_to_float(uint32_t u) {
 // Order-preserving key of the score of key j in this group (0 = no key: j >= Nk).
 __device__ inline uint32_t key_at(const float* srow, int j, int Nk) { return j < Nk ? order_key(srow[j]) : 0u; }
 
-constexpr int SEL_CAND = 4096;                                   // LDS candidates of the cut bin
+constexpr int SEL_CAND = 4096;                                   // LDS candidates around the cut
+constexpr int SEL_SAMPLE = 4096;                                 // sampled scores that locate the cut
 constexpr int SEL_UNROLL = 32;                                   // loads in flight per thread
 
 // In (digit-)bin search over hist[0..nb): the bin holding the kk-th largest element, counting from
@@ -244,6 +251,31 @@ __device__ inline void find_bin(const int* hist, int nb, int kk, int* wsum, int*
     }
   }
   __syncthreads();
+}
+
+// The key of rank `rank` (1 = largest) among keys[0..n) in LDS: 12 + 12 + 8 bit radix select.
+// Every thread of the block must call it; returns the same value in all threads.
+__device__ inline uint32_t lds_rank_select(const uint32_t* keys, int n, int rank, int* hist, int* wsum, int* found) {
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass], nb = 1 << widths[pass];
+    for (int bb = threadIdx.x; bb < nb; bb += SEL_THREADS) hist[bb] = 0;
+    if (threadIdx.x == 0) { found[0] = 0; found[1] = 1; }
+    __syncthreads();
+    for (int x = threadIdx.x; x < n; x += SEL_THREADS) {
+      const uint32_t u = keys[x];
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+    }
+    __syncthreads();
+    find_bin(hist, nb, rank, wsum, found);
+    prefix |= (uint32_t)found[0] << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+    rank = found[1];
+    __syncthreads();
+  }
+  return prefix;
 }
 
 // One 1024-thread workgroup per group.  Keys j are visited as rows i of 1024: j = 1024 i + tid, so a
@@ -287,28 +319,29 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
   int* cand_j = (int*)(cand_key + SEL_CAND);                       // SEL_CAND (top-k only)
 
   for (int w = tid; w < words; w += SEL_THREADS) { strict_bits[w] = 0u; tie_bits[w] = 0u; }
-  if (tid == 0) ncand = 0;
   int need = 0;
 
   if (TOPK) {
-    for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0;
-    if (tid == 0) { found[0] = 0; found[1] = 1; }
-    __syncthreads();
-    // pass 1: top 12 bits
-    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
-      uint32_t u[SEL_UNROLL];
-#pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
-#pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e)
-        if (u[e] != 0u) atomicAdd(&hist[u[e] >> 20], 1);
+    // ---- 1. a hashed sample of the scores, staged in the candidate buffer ----
+    const int S = Nk < SEL_SAMPLE ? Nk : SEL_SAMPLE;
+    for (int x = tid; x < S; x += SEL_THREADS) {
+      const int jj = S == Nk ? x : (int)(((uint64_t)(uint32_t)x * 2654435761ull) % (uint32_t)Nk);
+      cand_key[x] = key_at(srow, jj, Nk);
     }
     __syncthreads();
-    find_bin(hist, 4096, topk, wsum, found);
-    const uint32_t b1 = (uint32_t)found[0];
-    int kk = found[1];
+    // sample ranks (from the top) that bracket the cut with ~3.5 sigma of sampling error, and the
+    // sample keys at those ranks
+    const double pk = (double)topk / (double)Nk;
+    const int r = (int)ceil(pk * S);
+    const int delta = (int)ceil(3.5 * sqrt((double)S * pk * (1.0 - pk))) + 2;
+    const int r_hi = r - delta < 1 ? 1 : r - delta;
+    const int r_lo = r + delta > S ? S : r + delta;
+    const uint32_t key_hi = r_hi <= 1 && r - delta < 1 ? 0xffffffffu : lds_rank_select(cand_key, S, r_hi, hist, wsum, found);
+    const uint32_t key_lo = r_lo >= S && r + delta > S ? 1u : lds_rank_select(cand_key, S, r_lo, hist, wsum, found);
+    if (tid == 0) ncand = 0;
     __syncthreads();
-    // pass 2: keys above the cut bin -> strict bits; keys in it -> LDS candidates
+    // ---- 2. one pass: keys above the band -> strict bits; keys in it -> LDS candidates ----
+    int above_w = 0;   // keys above the band seen by this wave (lane 0)
     for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
       uint32_t u[SEL_UNROLL];
 #pragma unroll
@@ -317,30 +350,41 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
       for (int e = 0; e < SEL_UNROLL; ++e) {
         const int i = i0 + e;
         if (i < rows) {
-          const uint64_t above = __builtin_amdgcn_ballot_w64(u[e] != 0u && (u[e] >> 20) > b1);
+          const uint64_t above = __builtin_amdgcn_ballot_w64(u[e] > key_hi);
+          const bool cand = u[e] != 0u && u[e] >= key_lo && u[e] <= key_hi;
+          const uint64_t bc = __builtin_amdgcn_ballot_w64(cand);
+          int base = 0;
           if (lane == 0) {
             const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
             strict_bits[w0] = (uint32_t)above;
             strict_bits[w0 + 1] = (uint32_t)(above >> 32);
+            above_w += __popcll(above);
+            if (bc) base = atomicAdd(&ncand, (int)__popcll(bc));
           }
-          if (u[e] != 0u && (u[e] >> 20) == b1) {
-            const int pos = atomicAdd(&ncand, 1);
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (cand) {
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bc, 0u));
             if (pos < SEL_CAND) { cand_key[pos] = u[e]; cand_j[pos] = i * SEL_THREADS + tid; }
           }
         }
       }
     }
+    if (lane == 0) ired[wave] = above_w;
     __syncthreads();
+    int n_above = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) n_above += ired[w];
     const int nc = ncand;
-    uint32_t prefix = b1 << 20;
-    if (nc <= SEL_CAND) {
-      // lower digits on the LDS candidates
-      const int shifts[2] = {8, 0};
-      const int widths[2] = {12, 8};
-      uint32_t pmask = 0xfff00000u;
-      for (int pass = 0; pass < 2; ++pass) {
+    int kk = topk - n_above;
+    __syncthreads();
+    if (nc <= SEL_CAND && kk >= 1 && kk <= nc) {
+      // ---- 3. exact cut among the candidates: 12 + 12 + 8 bit radix select in LDS ----
+      const int shifts[3] = {20, 8, 0};
+      const int widths[3] = {12, 12, 8};
+      uint32_t prefix = 0, pmask = 0;
+      for (int pass = 0; pass < 3; ++pass) {
         const int sh = shifts[pass], nb = 1 << widths[pass];
-        for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
+        for (int bb = tid; bb < nb; bb += SEL_THREADS) hist[bb] = 0;
         if (tid == 0) { found[0] = 0; found[1] = 1; }
         __syncthreads();
         for (int x = tid; x < nc; x += SEL_THREADS) {
@@ -355,22 +399,22 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
         __syncthreads();
       }
       need = kk;
-      // candidates above the cut are kept; those equal to it are ties
       for (int x = tid; x < nc; x += SEL_THREADS) {
         const uint32_t u = cand_key[x];
-        const int j = cand_j[x];
-        if (u > prefix) atomicOr(&strict_bits[j >> 5], 1u << (j & 31));
-        else if (u == prefix) atomicOr(&tie_bits[j >> 5], 1u << (j & 31));
+        const int jj = cand_j[x];
+        if (u > prefix) atomicOr(&strict_bits[jj >> 5], 1u << (jj & 31));
+        else if (u == prefix) atomicOr(&tie_bits[jj >> 5], 1u << (jj & 31));
       }
       __syncthreads();
     } else {
-      // the cut bin is too crowded for LDS: resolve the lower digits from global memory
-      const int shifts[2] = {8, 0};
-      const int widths[2] = {12, 8};
-      uint32_t pmask = 0xfff00000u;
-      for (int pass = 0; pass < 2; ++pass) {
+      // ---- fallback: the sampled band missed the cut or overflowed: exact radix over global memory ----
+      const int shifts[3] = {20, 8, 0};
+      const int widths[3] = {12, 12, 8};
+      uint32_t prefix = 0, pmask = 0;
+      kk = topk;
+      for (int pass = 0; pass < 3; ++pass) {
         const int sh = shifts[pass], nb = 1 << widths[pass];
-        for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
+        for (int bb = tid; bb < nb; bb += SEL_THREADS) hist[bb] = 0;
         if (tid == 0) { found[0] = 0; found[1] = 1; }
         __syncthreads();
         for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
@@ -538,8 +582,8 @@ static int launch_mask_d(const MaskArgs& a) {
   int err = (int)hipGetLastError();
   if (err) return err;
   const int hp = mask_heads_per_pass(BH, G, a.Nk);
-  const int gtiles = (G + 31) / 32;
-  const int kchunks = (a.Nk + 4 * SC_KT * 32 - 1) / (4 * SC_KT * 32);
+  const int gtiles = (G + 127) / 128;                       // quads of 32-group tiles
+  const int kchunks = (a.Nk + SC_KT * 32 - 1) / (SC_KT * 32);
   const float log_tau = a.mode == 1 ? (a.thresh > 0.0f ? logf(a.thresh) : -INFINITY) : 0.0f;
   // dynamic LDS of the select kernel can exceed 64 KB (up to ~98 KB at the largest Nk)
   static bool lds_attr_set = false;
