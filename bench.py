@@ -47,6 +47,32 @@ def parse():
     return p.parse_args()
 
 
+FWD_SOURCES = ("sparse_self_attention_amd/csrc/attn_fwd.hip", "sparse_self_attention_amd/csrc/device_common.hpp")
+
+
+def fwd_source_hash() -> str:
+    """sha256 over the sources the sparse forward kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in FWD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per sparse-forward launch from the committed FETCH_SIZE / WRITE_SIZE counter summary,
+    or None when there is none for this workload or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != fwd_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def kept_flops(counts, w) -> float:
     """4 D sum_{b,h,g} |g| c_g: QK^T and PV multiply-adds over the kept (query, key) pairs."""
     import numpy as np
@@ -191,9 +217,9 @@ def main():
         "gathered_GBps_fwd": round(float(cnt_h.sum()) * 2 * w.dim * 2 / (fwd_avg * 1e-3) / 1e9, 1),
     }
     # dominant kernel: the sparse forward (one launch per step)
-    rec["roofline"] = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,4,sparse,bf16>",
+    rec["roofline"] = {"bound": "mfma", "kernel": f"attn_fwd_lean<{w.dim},sparse,bf16>",
                        "achieved": round(fwd_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                       "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                       "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(w.name)}
     if args.copy_calibration_mib > 0:
         src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -10,12 +10,13 @@
 //  k_scores       s[g, j] = scale * (hi_g . k_j + lo_g . k_j) with v_mfma_f32_32x32x16_bf16, in tiles
 //                 of 128 groups x 32 keys so every K row read feeds 128 groups; fp32 scores of a bounded
 //                 number of heads are staged in the workspace (sized to stay in the 256 MB MALL).
-//  k_select       one 1024-thread workgroup per group.  Top-k: a histogram of a hashed sample of
-//                 4096 scores locates the cut to within ~3.5 sigma of sampling error; one pass over the
-//                 staged scores marks the keys above that band and copies the keys inside it to LDS,
-//                 where a 12 + 12 + 8 bit radix select finds the exact k-th largest (ties go to the
-//                 lowest key index).  If the band misses the cut or overflows LDS, the cut is found
-//                 by radix passes over the staged scores instead.  Threshold: block max + block sum
+//  k_select       one 1024-thread workgroup per group.  Top-k: the scores kernel also writes every
+//                 16th score of a row to a short sample row; the sample's order statistics bracket
+//                 the cut to within ~3.5 sigma of sampling error.  One pass over the staged scores
+//                 marks the keys above that band and copies the keys inside it to LDS, where a
+//                 12 + 12 + 8 bit radix select finds the exact k-th largest (ties go to the lowest
+//                 key index).  If the band misses the cut or overflows LDS, the cut is found by
+//                 radix passes over the staged scores instead.  Threshold: block max + block sum
 //                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Keep flags live in
 //                 LDS bitmaps written by wave ballots; the ascending list is written from popcounts,
 //                 one block scan and mbcnt.
@@ -34,6 +35,10 @@ constexpr int SEL_WAVES = SEL_THREADS / 64;
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // fp32 score rows are padded to a multiple of 4 floats so 16-byte stores stay aligned
 static inline __host__ __device__ int score_stride(int Nk) { return (Nk + 3) & ~3; }
+// Every SAMPLE_STEP-th score of a row is also written to a short contiguous sample row.
+constexpr int SAMPLE_STEP = 16;
+static inline __host__ __device__ int sample_len(int Nk) { return (Nk + SAMPLE_STEP - 1) / SAMPLE_STEP; }
+static inline __host__ __device__ int sample_stride(int Nk) { return (sample_len(Nk) + 3) & ~3; }
 
 int mask_heads_per_pass(int BH, int G, int Nk) {
   const size_t per = (size_t)G * (size_t)score_stride(Nk) * 4;
@@ -45,8 +50,10 @@ int mask_heads_per_pass(int BH, int G, int Nk) {
 
 size_t mask_workspace_bytes(int BH, int G, int Nk, int D) {
   const size_t means = align256((size_t)BH * G * D * 2);
-  const size_t scores = align256((size_t)mask_heads_per_pass(BH, G, Nk) * G * score_stride(Nk) * 4);
-  return 2 * means + scores;
+  const size_t hp = (size_t)mask_heads_per_pass(BH, G, Nk);
+  const size_t scores = align256(hp * G * score_stride(Nk) * 4);
+  const size_t samples = align256(hp * G * sample_stride(Nk) * 4);
+  return 2 * means + scores + samples;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -99,9 +106,10 @@ constexpr int SC_KT = 8;   // 32-key tiles per workgroup
 // fetched once per workgroup.  In the accumulator layout lane l holds key j0 + l%32 for 16 groups:
 // each store instruction writes two contiguous 128-byte runs of score rows.
 template <int D>
-__global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, const uint16_t* __restrict__ qhi,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_scores(const uint16_t* __restrict__ k, const uint16_t* __restrict__ qhi,
                                                  const uint16_t* __restrict__ qlo, int Nk, int G, float scale,
-                                                 float* __restrict__ scores, int bh0, int gtiles, int kchunks) {
+                                                 float* __restrict__ scores, float* __restrict__ samples, int bh0,
+                                                 int gtiles, int kchunks) {
   constexpr int KSTEPS = D / 16;
   constexpr int RB = D * 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -127,6 +135,9 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, 
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * Nk * D, (uint32_t)Nk * RB);
   const int stride = score_stride(Nk);
   float* sbase = scores + (size_t)hh * G * stride;
+  const int sstride = sample_stride(Nk);
+  float* pbase = samples + (size_t)hh * G * sstride;
+  const bool sampler = (ql % SAMPLE_STEP) == 0;   // j0 is a multiple of 32, so j % 16 == ql % 16
   for (int kt = 0; kt < SC_KT; ++kt) {
     const int j0 = (kc * SC_KT + kt) * 32;
     if (j0 >= Nk) break;
@@ -146,7 +157,11 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t* __restrict__ k, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int g = gt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (g < G) sbase[(size_t)g * stride + j] = acc[r] * scale;
+        if (g < G) {
+          const float sv = acc[r] * scale;
+          sbase[(size_t)g * stride + j] = sv;
+          if (sampler) pbase[(size_t)g * sstride + j / SAMPLE_STEP] = sv;
+        }
       }
     }
   }
@@ -225,8 +240,7 @@ __device__ inline float key_to_float(uint32_t u) {
 __device__ inline uint32_t key_at(const float* srow, int j, int Nk) { return j < Nk ? order_key(srow[j]) : 0u; }
 
 constexpr int SEL_CAND = 4096;                                   // LDS candidates around the cut
-constexpr int SEL_SAMPLE = 4096;                                 // sampled scores that locate the cut
-constexpr int SEL_UNROLL = 32;                                   // loads in flight per thread
+constexpr int SEL_UNROLL = 16;                                   // loads in flight per thread
 
 // In (digit-)bin search over hist[0..nb): the bin holding the kk-th largest element, counting from
 // the top.  Thread t owns bins nb-1-per*t ... (descending); writes found[0] = bin, found[1] = rank
@@ -253,38 +267,42 @@ __device__ inline void find_bin(const int* hist, int nb, int kk, int* wsum, int*
   __syncthreads();
 }
 
-// The key of rank `rank` (1 = largest) among keys[0..n) in LDS: 12 + 12 + 8 bit radix select.
-// Every thread of the block must call it; returns the same value in all threads.
-__device__ inline uint32_t lds_rank_select(const uint32_t* keys, int n, int rank, int* hist, int* wsum, int* found) {
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  uint32_t prefix = 0, pmask = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = 1 << widths[pass];
-    for (int bb = threadIdx.x; bb < nb; bb += SEL_THREADS) hist[bb] = 0;
-    if (threadIdx.x == 0) { found[0] = 0; found[1] = 1; }
-    __syncthreads();
-    for (int x = threadIdx.x; x < n; x += SEL_THREADS) {
-      const uint32_t u = keys[x];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+// Like find_bin for two ranks at once: kA among the counts hA, kB among hB (hA may equal hB).  Each
+// distribution holds fewer than 65536 elements, so the two counts travel packed in one int through a
+// single block scan.  Writes found[0..1] = (bin, rank inside) for A and found[2..3] for B.
+__device__ inline void find_bin_pair(const int* hA, const int* hB, int nb, int kA, int kB, int* wsum, int* found) {
+  const int tid = threadIdx.x;
+  const int per = nb / SEL_THREADS > 0 ? nb / SEL_THREADS : 1;
+  const bool owner = tid * per < nb;
+  int local = 0;
+  if (owner)
+    for (int e = 0; e < per; ++e) {
+      const int b = nb - 1 - (tid * per + e);
+      local += hA[b] + (hB[b] << 16);
     }
-    __syncthreads();
-    find_bin(hist, nb, rank, wsum, found);
-    prefix |= (uint32_t)found[0] << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
-    rank = found[1];
-    __syncthreads();
+  int total;
+  const int above = block_excl_scan(local, wsum, total);
+  if (owner) {
+    int aA = above & 0xffff, aB = above >> 16;
+    for (int e = 0; e < per; ++e) {
+      const int b = nb - 1 - (tid * per + e);
+      const int cA = hA[b], cB = hB[b];
+      if (aA < kA && kA <= aA + cA) { found[0] = b; found[1] = kA - aA; }
+      if (aB < kB && kB <= aB + cB) { found[2] = b; found[3] = kB - aB; }
+      aA += cA;
+      aB += cB;
+    }
   }
-  return prefix;
+  __syncthreads();
 }
 
 // One 1024-thread workgroup per group.  Keys j are visited as rows i of 1024: j = 1024 i + tid, so a
 // wave covers 64 consecutive keys of a row and its ballot is one 64-bit word pair of a bitmap.
-//  top-k:     pass 1 (global) 12-bit histogram of the top digit; pass 2 (global) marks keys above the
-//             cut bin in `strict` and copies the cut bin's keys to LDS; the lower 20 bits are resolved
-//             on those candidates (12 + 8 bit digits); candidates above the cut join `strict`, ties
-//             at the cut go to `tie`.  If the cut bin overflows the LDS list, passes 2-3 and the
-//             flags are computed from global memory instead.
+//  top-k:     the sample locates a band [key_lo, key_hi] around the cut; one pass (global) marks the
+//             keys above it in `strict` and copies the band's keys to LDS; an exact radix select on
+//             them resolves the cut; candidates above it join `strict`, ties at the cut go to `tie`.
+//             If the band misses the cut or overflows the LDS list, the cut and the flags are
+//             computed from global memory instead.
 //  threshold: pass 1 max, pass 2 sum of exp, pass 3 marks s >= lse + ln tau in `strict`.
 //  Compaction: popcounts of the bitmap words per (row, wave), one block scan, then each kept key
 //  writes its index at its rank; ties are taken lowest index first up to `need`.
@@ -294,15 +312,17 @@ static inline size_t select_lds_bytes(int Nk, bool topk) {
   return 4 * ((topk ? 4096 : 0) + 2 * words + 2 * rows * SEL_WAVES + (topk ? 2 * SEL_CAND : 0));
 }
 
+// 2 workgroups per CU: at most 64 VGPRs (8 waves per SIMD).
 template <bool TOPK>
-__global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict__ scores, int Nk, int G, int topk,
+__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_select(const float* __restrict__ scores, const float* __restrict__ samples, int Nk, int G, int topk,
                                                         float log_tau, int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ counts, int cap, int bh0) {
   extern __shared__ __attribute__((aligned(16))) int sel_dyn[];   // sized by select_lds_bytes(Nk, TOPK)
   __shared__ int wsum[SEL_WAVES];
   __shared__ float fred[SEL_WAVES];
   __shared__ int ired[SEL_WAVES];
-  __shared__ int found[2];
+  __shared__ int found[4];
   __shared__ int ncand;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = blockIdx.x / G, g = blockIdx.x % G;
@@ -322,22 +342,43 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
   int need = 0;
 
   if (TOPK) {
-    // ---- 1. a hashed sample of the scores, staged in the candidate buffer ----
-    const int S = Nk < SEL_SAMPLE ? Nk : SEL_SAMPLE;
-    for (int x = tid; x < S; x += SEL_THREADS) {
-      const int jj = S == Nk ? x : (int)(((uint64_t)(uint32_t)x * 2654435761ull) % (uint32_t)Nk);
-      cand_key[x] = key_at(srow, jj, Nk);
+    // ---- 1. the cut's neighbourhood, from the every-16th-key sample of the row ----
+    // Keys above key_hi are kept outright; keys in [key_lo, key_hi] become LDS candidates.  The bounds
+    // are the sample's order statistics ~3.5 sigma of sampling error either side of the cut's rank,
+    // each resolved to 23 of 32 key bits and rounded outwards.  Rows short enough to fit the
+    // candidate list skip this: every key is a candidate.
+    uint32_t key_hi = 0xffffffffu, key_lo = 1u;
+    if (Nk > SEL_CAND) {
+      const int S = sample_len(Nk);               // <= 2 * SEL_CAND: cand_key and cand_j are contiguous
+      uint32_t* skey = cand_key;
+      const float* prow = samples + ((size_t)hh * G + g) * sample_stride(Nk);
+      for (int x = tid; x < S; x += SEL_THREADS) skey[x] = order_key(prow[x]);
+      for (int bb = tid; bb < 4096; bb += SEL_THREADS) hist[bb] = 0;
+      __syncthreads();
+      const double pk = (double)topk / (double)Nk;
+      const int r = (int)ceil(pk * S);
+      const int delta = (int)ceil(3.5 * sqrt((double)S * pk * (1.0 - pk))) + 2;
+      const bool open_hi = r - delta < 1, open_lo = r + delta > S;
+      const int r_hi = open_hi ? 1 : r - delta;
+      const int r_lo = open_lo ? S : r + delta;
+      for (int x = tid; x < S; x += SEL_THREADS) atomicAdd(&hist[skey[x] >> 20], 1);
+      __syncthreads();
+      find_bin_pair(hist, hist, 4096, r_hi, r_lo, wsum, found);
+      const uint32_t bA = (uint32_t)found[0], bB = (uint32_t)found[2];
+      const int kA = found[1], kB = found[3];
+      __syncthreads();
+      for (int bb = tid; bb < 4096; bb += SEL_THREADS) hist[bb] = 0;
+      __syncthreads();
+      for (int x = tid; x < S; x += SEL_THREADS) {
+        const uint32_t u = skey[x], top = u >> 20, sub = (u >> 9) & 2047u;
+        if (top == bA) atomicAdd(&hist[sub], 1);
+        if (top == bB) atomicAdd(&hist[2048 + sub], 1);
+      }
+      __syncthreads();
+      find_bin_pair(hist, hist + 2048, 2048, kA, kB, wsum, found);
+      if (!open_hi) key_hi = (bA << 20) | ((uint32_t)found[0] << 9) | 0x1ffu;
+      if (!open_lo) key_lo = max(1u, (bB << 20) | ((uint32_t)found[2] << 9));
     }
-    __syncthreads();
-    // sample ranks (from the top) that bracket the cut with ~3.5 sigma of sampling error, and the
-    // sample keys at those ranks
-    const double pk = (double)topk / (double)Nk;
-    const int r = (int)ceil(pk * S);
-    const int delta = (int)ceil(3.5 * sqrt((double)S * pk * (1.0 - pk))) + 2;
-    const int r_hi = r - delta < 1 ? 1 : r - delta;
-    const int r_lo = r + delta > S ? S : r + delta;
-    const uint32_t key_hi = r_hi <= 1 && r - delta < 1 ? 0xffffffffu : lds_rank_select(cand_key, S, r_hi, hist, wsum, found);
-    const uint32_t key_lo = r_lo >= S && r + delta > S ? 1u : lds_rank_select(cand_key, S, r_lo, hist, wsum, found);
     if (tid == 0) ncand = 0;
     __syncthreads();
     // ---- 2. one pass: keys above the band -> strict bits; keys in it -> LDS candidates ----
@@ -378,24 +419,26 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
     int kk = topk - n_above;
     __syncthreads();
     if (nc <= SEL_CAND && kk >= 1 && kk <= nc) {
-      // ---- 3. exact cut among the candidates: 12 + 12 + 8 bit radix select in LDS ----
-      const int shifts[3] = {20, 8, 0};
-      const int widths[3] = {12, 12, 8};
-      uint32_t prefix = 0, pmask = 0;
-      for (int pass = 0; pass < 3; ++pass) {
-        const int sh = shifts[pass], nb = 1 << widths[pass];
+      // ---- 3. exact cut among the candidates: radix select in LDS over the low `bits` key bits,
+      // the ones that still vary inside [key_lo, key_hi] (the bits above are common to all) ----
+      const uint32_t diff = key_lo ^ key_hi;
+      int bits = diff ? 32 - __clz(diff) : 0;
+      uint32_t prefix = bits == 32 ? 0u : (key_hi >> bits) << bits;
+      while (bits > 0) {
+        const int w = bits > 12 ? 12 : bits;
+        const int sh = bits - w, nb = 1 << w;
         for (int bb = tid; bb < nb; bb += SEL_THREADS) hist[bb] = 0;
         if (tid == 0) { found[0] = 0; found[1] = 1; }
         __syncthreads();
         for (int x = tid; x < nc; x += SEL_THREADS) {
           const uint32_t u = cand_key[x];
-          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+          if (((uint64_t)(u ^ prefix) >> bits) == 0) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
         }
         __syncthreads();
         find_bin(hist, nb, kk, wsum, found);
         prefix |= (uint32_t)found[0] << sh;
-        pmask |= (uint32_t)(nb - 1) << sh;
         kk = found[1];
+        bits = sh;
         __syncthreads();
       }
       need = kk;
@@ -525,6 +568,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
   int32_t* out = idx + unit * (size_t)cap;
   const int kept = tot_s + min(tot_t, need);
   if (kept > 0) {
+#pragma unroll 4
     for (int i = 0; i < rows; ++i) {
       const int x = i * SEL_WAVES + wave;
       const uint64_t bs = (uint64_t)strict_bits[2 * x] | ((uint64_t)strict_bits[2 * x + 1] << 32);
@@ -577,11 +621,12 @@ static int launch_mask_d(const MaskArgs& a) {
   uint16_t* qhi = (uint16_t*)ws;
   uint16_t* qlo = (uint16_t*)(ws + means);
   float* scores = (float*)(ws + 2 * means);
+  const int hp = mask_heads_per_pass(BH, G, a.Nk);
+  float* samples = (float*)(ws + 2 * means + align256((size_t)hp * G * score_stride(a.Nk) * 4));
   hipLaunchKernelGGL((k_group_mean<D>), dim3(BH * G), dim3(256), 0, st, (const uint16_t*)a.q, a.Nq, a.group, G,
                      qhi, qlo);
   int err = (int)hipGetLastError();
   if (err) return err;
-  const int hp = mask_heads_per_pass(BH, G, a.Nk);
   const int gtiles = (G + 127) / 128;                       // quads of 32-group tiles
   const int kchunks = (a.Nk + SC_KT * 32 - 1) / (SC_KT * 32);
   const float log_tau = a.mode == 1 ? (a.thresh > 0.0f ? logf(a.thresh) : -INFINITY) : 0.0f;
@@ -598,10 +643,10 @@ static int launch_mask_d(const MaskArgs& a) {
   for (int bh0 = 0; bh0 < BH; bh0 += hp) {
     const int n = BH - bh0 < hp ? BH - bh0 : hp;
     hipLaunchKernelGGL((k_scores<D>), dim3(n * gtiles * kchunks), dim3(256), 0, st, (const uint16_t*)a.k, qhi, qlo,
-                       a.Nk, G, a.scale, scores, bh0, gtiles, kchunks);
+                       a.Nk, G, a.scale, scores, samples, bh0, gtiles, kchunks);
 #define SATTN_SEL(T_)                                                                                     \
   hipLaunchKernelGGL((k_select<T_>), dim3(n * G), dim3(SEL_THREADS), select_lds_bytes(a.Nk, T_), st, scores,    \
-                     a.Nk, G, a.topk, log_tau, a.idx, a.counts, a.cap, bh0)
+                     samples, a.Nk, G, a.topk, log_tau, a.idx, a.counts, a.cap, bh0)
     if (a.mode == 0) SATTN_SEL(true);
     else SATTN_SEL(false);
 #undef SATTN_SEL
