@@ -9,7 +9,8 @@
 //                 so the matrix cores score with about 16 mantissa bits of the mean.
 //  k_scores       s[g, j] = scale * (hi_g . k_j + lo_g . k_j) with v_mfma_f32_32x32x16_bf16, in tiles
 //                 of 128 groups x 32 keys so every K row read feeds 128 groups; fp32 scores of a bounded
-//                 number of heads are staged in the workspace (sized to stay in the 256 MB MALL).
+//                 number of heads are staged in the workspace (up to 1 GB, so one select launch
+//                 spans several heads and fills the GPU).
 //  k_select       one 1024-thread workgroup per group.  Top-k: the scores kernel also writes every
 //                 16th score of a row to a short sample row; the sample's order statistics bracket
 //                 the cut to within ~3.5 sigma of sampling error.  One pass over the staged scores
@@ -28,7 +29,7 @@
 
 namespace sattn {
 
-constexpr size_t SCORE_STAGE_BUDGET = 200ull << 20;   // bytes of fp32 scores staged per pass (MALL-sized)
+constexpr size_t SCORE_STAGE_BUDGET = 1024ull << 20;  // bytes of fp32 scores staged per pass
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 
