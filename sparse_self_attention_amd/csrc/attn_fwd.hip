@@ -9,7 +9,7 @@
 // Mapping onto CDNA4
 // ------------------
 //  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32) of the group.
-//  * Key blocks of BK = 64 kept keys.  The block's K and V rows are gathered from HBM straight
+//  * Key blocks of 32 kept keys.  The block's K and V rows are gathered from HBM straight
 //    into LDS with 16-byte buffer-load-to-LDS instructions (one lane = one 16 B chunk of a row),
 //    double-buffered so the gather of block j+1 overlaps the math of block j.  Buffer loads
 //    return zeros for an out-of-range row instead of faulting.
@@ -22,10 +22,10 @@
 //    accumulators also have one query per lane and the rescale by exp(m_old - m_new) is a
 //    per-lane multiply.
 //  * The softmax runs in base 2 with log2(e) folded into the score scale.  The running max is
-//    only moved when a block's max exceeds it by more than 2^8; until then probabilities may
-//    exceed 1 by at most 2^8, which fp32 and bf16 carry exactly as well.  The row sum adds the
-//    bf16-rounded probabilities that also feed the PV product, so every output row is a convex
-//    combination of the kept V rows with weights that sum to one.
+//    taken from the first block and moved only when a later block's probabilities could exceed
+//    2^64 (checked through the block's partial row sums; an overflow trips the same check), so
+//    the common path has no max reduction and no rescale.  P enters the PV product rounded to
+//    bf16; the row sum adds the fp32 probabilities.
 //  * LDS rows are XOR-swizzled in 16-byte chunks: K rows so that 16 consecutive rows read at
 //    the same chunk hit distinct banks, V rows so that the 4-row transposed reads do.
 #include <stdlib.h>
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r + 1], scale_log2, -m_run));
         pk[r >> 1] = pack_bf16x2(p0, p1);
-        lsum = add_bf16x2(pk[r >> 1], lsum);
+        lsum += p0 + p1;   // plain fp32 adds: a dot2 row sum would stall on the running MFMAs
       }
     };
     if (j == 0) take_max();
