@@ -16,8 +16,12 @@ Readings of passages that the pages leave open:
     the lost softmax denominator: a key is skipped when its pooled softmax
     probability is below tau;
   * a group with no kept keys outputs zeros and lse = -inf;
-  * top-k ties go to the lowest key index; index lists are ascending.
+  * top-k ties go to the lowest key index; index lists are ascending;
+  * the cached mask keeps slice (g, j) when some query of group g gives key j a
+    full-attention softmax probability of at least tau; tau <= 0 keeps every
+    key and a group may keep none.
 """
 from .attention import dense_attention_ref, sparse_attention_ref, sparse_attention_probs_ref  # noqa: F401
 from .mask import (group_mean_ref, group_scores_ref, topk_select_ref, thresh_select_ref,  # noqa: F401
                    mask_ref)
+from .cached import row_lse_ref, slice_max_logprob_ref, cached_mask_ref  # noqa: F401

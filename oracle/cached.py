@@ -1,0 +1,86 @@
+"""fp64 oracle of the cached (full-attention) slice mask.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+library path.
+
+FG-Attn review, Figure 10: during a dense denoising iteration the full attention
+scores are evaluated, and an M x 1 slice (the M queries of a group against one
+key) is marked when at least one of its scores is above a threshold tau_cached;
+the mask is stored and reused by later iterations.  The review's list of free
+parameters sets tau_cached = 0.5 / N (N = sequence length), so the "score" is a
+softmax probability: slice (g, j) is kept iff
+
+    max over queries i of group g of  p_ij = exp(scale q_i . k_j - lse_i)  >=  tau,
+
+with lse_i the log-sum-exp of query i's scaled scores over all keys.  The same
+review (Referee major comment 2 and its suggested test) uses this slice set as
+the ground truth for the recall of the pooled mask.
+
+Readings where the pages are silent: tau <= 0 keeps every key; a group whose
+probabilities all fall below tau keeps no key (count 0); lists are ascending.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def row_lse_ref(q, k, scale: float) -> np.ndarray:
+    """lse[b,h,i] = log sum_j exp(scale q_i . k_j) over all keys (natural log), fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) * scale
+    m = s.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(s - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def slice_max_logprob_ref(q, k, group: int, scale: float, lse=None, units=None) -> dict:
+    """m[(b,h,g)][j] = max over the group's queries i of (scale q_i . k_j - lse_i).
+
+    lse defaults to the exact fp64 row log-sum-exp.  units: optional list of (b, h, g) to evaluate
+    (default: all).  Returns {(b, h, g): row of length Nk}.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, Nq, D = q.shape
+    G = -(-Nq // group)
+    if units is None:
+        units = [(b, h, g) for b in range(B) for h in range(H) for g in range(G)]
+    out = {}
+    for b, h, g in units:
+        r0, r1 = g * group, min((g + 1) * group, Nq)
+        s = np.matmul(q[b, h, r0:r1], k[b, h].T) * scale                  # [rows, Nk]
+        if lse is None:
+            mx = s.max(axis=1, keepdims=True)
+            l_rows = (mx + np.log(np.exp(s - mx).sum(axis=1, keepdims=True)))[:, 0]
+        else:
+            l_rows = np.asarray(lse, dtype=np.float64)[b, h, r0:r1]
+        out[(b, h, g)] = (s - l_rows[:, None]).max(axis=0)
+    return out
+
+
+def cached_mask_ref(q, k, group: int, tau: float, scale: float = None, lse=None, cap: int = None) -> dict:
+    """Full cached-mask oracle: idx [B,H,G,cap] (ascending, -1 past counts), counts [B,H,G] and the
+    per-slice max log-probability m [B,H,G,Nk]; log_tau = ln(tau) (-inf for tau <= 0)."""
+    q = np.asarray(q)
+    B, H, Nq, D = q.shape
+    Nk = np.asarray(k).shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    G = -(-Nq // group)
+    if cap is None:
+        cap = Nk
+    rows = slice_max_logprob_ref(q, k, group, scale, lse=lse)
+    log_tau = -math.inf if tau <= 0.0 else math.log(tau)
+    idx = np.full((B, H, G, cap), -1, dtype=np.int32)
+    counts = np.zeros((B, H, G), dtype=np.int32)
+    m = np.empty((B, H, G, Nk))
+    for (b, h, g), row in rows.items():
+        kept = np.nonzero(row >= log_tau)[0]
+        if kept.size > cap:
+            raise ValueError("cap too small for the kept key list")
+        idx[b, h, g, :kept.size] = kept
+        counts[b, h, g] = kept.size
+        m[b, h, g] = row
+    return {"idx": idx, "counts": counts, "m": m, "log_tau": log_tau}

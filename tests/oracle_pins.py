@@ -266,3 +266,100 @@ def check_thresh(thresh_select):
     s = np.array([1.0, 3.0, 3.0, 2.0])
     kept, _ = thresh_select(s, 0.99)
     assert list(kept) == [1], "arg-max fallback: lowest index on ties"
+
+
+# ----------------------------------------------------------------------------
+# cached (full-attention) slice mask
+# ----------------------------------------------------------------------------
+
+def _brute_slice_keep(q, k, group, tau, scale):
+    """Pure-Python loops: p_ij = exp(s_ij - lse_i) with fsum; slice (g, j) kept iff max_i p_ij >= tau.
+    Returns (keep[b][h][g][j] booleans, min distance of any p_ij from tau)."""
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    G = -(-Nq // group)
+    keep = np.zeros((B, H, G, Nk), dtype=bool)
+    gap = math.inf
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                s = [math.fsum(float(q[b, h, i, d]) * float(k[b, h, j, d]) for d in range(D)) * scale
+                     for j in range(Nk)]
+                m = max(s)
+                lse = m + math.log(math.fsum(math.exp(x - m) for x in s))
+                for j in range(Nk):
+                    p = math.exp(s[j] - lse)
+                    gap = min(gap, abs(p - tau))
+                    if p >= tau:
+                        keep[b, h, i // group, j] = True
+    return keep, gap
+
+
+def _kept_sets(res):
+    B, H, G = res["counts"].shape
+    return {(b, h, g): set(res["idx"][b, h, g, :res["counts"][b, h, g]].tolist())
+            for b in range(B) for h in range(H) for g in range(G)}
+
+
+def check_cached_brute_force(cached):
+    """Tiny cases against explicit per-query probabilities."""
+    rng = np.random.default_rng(21)
+    for (B, H, Nq, Nk, D, M) in [(1, 2, 10, 13, 4, 4), (2, 1, 7, 9, 3, 3), (1, 1, 6, 11, 5, 1)]:
+        q, k, _ = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=2.0)
+        scale = 1.0 / math.sqrt(D)
+        for tau in (0.5 / Nk, 1.0 / Nk, 0.2, 0.6):
+            keep, gap = _brute_slice_keep(q, k, M, tau, scale)
+            if gap < 1e-9:
+                continue
+            res = cached(q, k, M, tau, scale)
+            sets = _kept_sets(res)
+            for (b, h, g), got in sets.items():
+                want = set(np.nonzero(keep[b, h, g])[0].tolist())
+                assert got == want, ((b, h, g), tau, sorted(got ^ want))
+                lst = res["idx"][b, h, g, :res["counts"][b, h, g]]
+                assert np.all(np.diff(lst) > 0)
+
+
+def check_cached_properties(cached, row_lse):
+    """lse against scipy; tau <= 0 keeps all; tau > 1 keeps none; uniform attention; monotone in tau;
+    each query's arg-max key survives tau <= 1/Nk; single-query groups threshold that query."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(23)
+    B, H, Nq, Nk, D, M = 1, 2, 24, 40, 8, 8
+    q, k, _ = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=3.0)
+    scale = 1.0 / math.sqrt(D)
+    s = np.einsum("bhid,bhjd->bhij", q, k) * scale
+    assert np.allclose(row_lse(q, k, scale), logsumexp(s, axis=-1), rtol=0, atol=TOL)
+    G = Nq // M
+    allk = cached(q, k, M, 0.0, scale)
+    assert np.all(allk["counts"] == Nk)
+    none = cached(q, k, M, 1.0 + 1e-6, scale)
+    assert np.all(none["counts"] == 0)
+    prev = None
+    for tau in (1e-4, 0.5 / Nk, 1.0 / Nk, 0.05, 0.3):
+        cur = _kept_sets(cached(q, k, M, tau, scale))
+        if prev is not None:
+            assert all(cur[u] <= prev[u] for u in cur)
+        prev = cur
+    # every query's arg-max key has p >= 1/Nk
+    sets = _kept_sets(cached(q, k, M, 1.0 / Nk, scale))
+    am = s.argmax(axis=-1)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                assert int(am[b, h, i]) in sets[(b, h, i // M)]
+    # uniform attention: identical keys give p = 1/Nk everywhere
+    ku = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    assert np.all(cached(q, ku, M, 0.5 / Nk, scale)["counts"] == Nk)
+    assert np.all(cached(q, ku, M, 1.5 / Nk, scale)["counts"] == 0)
+    # single-query groups: the slice set is that query's own thresholded probabilities
+    p = np.exp(s - logsumexp(s, axis=-1, keepdims=True))
+    one = _kept_sets(cached(q, k, 1, 0.05, scale))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                assert one[(b, h, i)] == set(np.nonzero(p[b, h, i] >= 0.05)[0].tolist())
+    # an explicit lse gives the same sets as the default exact one
+    lse = row_lse(q, k, scale)
+    assert _kept_sets(cached(q, k, M, 0.03, scale, lse=lse)) == _kept_sets(cached(q, k, M, 0.03, scale))
+    assert G * M == Nq

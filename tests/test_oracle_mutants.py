@@ -70,6 +70,28 @@ MASK_MUTANTS = [
 ]
 
 
+CACHED_MUTANTS = [
+    ("min over the group's queries", "out[(b, h, g)] = (s - l_rows[:, None]).max(axis=0)",
+     "out[(b, h, g)] = (s - l_rows[:, None]).min(axis=0)"),
+    ("lse not subtracted", "out[(b, h, g)] = (s - l_rows[:, None]).max(axis=0)", "out[(b, h, g)] = s.max(axis=0)"),
+    ("lse over the queries", "mx = s.max(axis=1, keepdims=True)\n            l_rows = (mx + np.log(np.exp(s - mx).sum(axis=1, keepdims=True)))[:, 0]",
+     "mx = s.max(axis=0, keepdims=True)\n            l_rows = (mx + np.log(np.exp(s - mx).sum(axis=0, keepdims=True)))[0, :s.shape[0]]"),
+    ("score scale dropped", "s = np.matmul(q[b, h, r0:r1], k[b, h].T) * scale", "s = np.matmul(q[b, h, r0:r1], k[b, h].T)"),
+    ("group rows shifted", "r0, r1 = g * group, min((g + 1) * group, Nq)\n        s =",
+     "r0, r1 = max(g * group - 1, 0), min((g + 1) * group, Nq) - (1 if g else 0)\n        s ="),
+    ("wrong sign of ln tau", "log_tau = -math.inf if tau <= 0.0 else math.log(tau)", "log_tau = -math.inf if tau <= 0.0 else -math.log(tau)"),
+    ("row lse without the max term", "return (m + np.log(", "return (np.log("),
+]
+
+
+@pytest.mark.parametrize("name,old,new", CACHED_MUTANTS, ids=[m[0] for m in CACHED_MUTANTS])
+def test_cached_mutant_is_caught(name, old, new):
+    m = _mutant("oracle.cached", old, new)
+    checks = [lambda: pins.check_cached_brute_force(m.cached_mask_ref),
+              lambda: pins.check_cached_properties(m.cached_mask_ref, m.row_lse_ref)]
+    assert _caught(checks), f"no pin catches the planted mistake: {name}"
+
+
 @pytest.mark.parametrize("name,old,new", FWD_MUTANTS, ids=[m[0] for m in FWD_MUTANTS])
 def test_forward_mutant_is_caught(name, old, new):
     m = _mutant("oracle.attention", old, new)
