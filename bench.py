@@ -112,6 +112,17 @@ def cpu_baseline(w, qb, kb, vb, idx_h, cnt_h, n_units):
                       f"one process per core, {dt:.1f} s wall"}
 
 
+def _slice_bitmap(idx, counts, n_k):
+    """[G, n_k] bool device tensor of the kept (group, key) slices of one head's lists."""
+    import torch
+    G, cap = idx.shape
+    valid = torch.arange(cap, device=idx.device)[None, :] < counts[:, None].long()
+    cols = torch.where(valid, idx.long(), torch.full_like(idx, n_k, dtype=torch.long))
+    m = torch.zeros((G, n_k + 1), dtype=torch.bool, device=idx.device)
+    m.scatter_(1, cols, True)
+    return m[:, :n_k]
+
+
 def _oracle_unit(job):
     import numpy as np
     from oracle import sparse_attention_ref
@@ -242,6 +253,31 @@ def main():
         rec["dense_tflops"] = round(dflops / (dense_ms * 1e-3) / 1e12, 2)
         rec["speedup_vs_dense_fwd"] = round(dense_ms / fwd_avg, 3)
         rec["speedup_vs_dense_job"] = round(dense_ms / (total_ms / steps), 3)
+        # cached slice mask of a dense step (tau = 0.5 / N on the lse that the dense pass returns), and
+        # the recall of the step-0 pooled top-k lists against it (the pages' suggested mask check)
+        sattn.attn(q0, k0, v, out=out, lse=lse)
+        cidx = torch.empty((1, w.heads, G, w.n_k), dtype=torch.int32, device=dev)
+        ccnt = torch.empty((1, w.heads, G), dtype=torch.int32, device=dev)
+        cms = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sattn.cached_mask(q0, k0, lse, w.group, idx=cidx, counts=ccnt)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cms.append(a.elapsed_time(b))
+        sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
+        torch.cuda.synchronize()
+        hit = tot = 0
+        for h in range(w.heads):
+            cm = _slice_bitmap(cidx[0, h], ccnt[0, h], w.n_k)
+            pm = _slice_bitmap(idx[0, h], counts[0, h], w.n_k)
+            hit += int((cm & pm).sum())
+            tot += int(cm.sum())
+        rec["cached_mask"] = {"ms": round(float(np.median(cms)), 3), "tau": 0.5 / w.n_k,
+                              "density": round(tot / (w.heads * G * w.n_k), 4),
+                              "pooled_topk_recall": round(hit / max(tot, 1), 4)}
+        del cidx, ccnt
     if not args.no_cpu_baseline and not args.kernel_only:
         # oracle on the step-0 inputs with the step-0 lists
         sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)

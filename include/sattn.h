@@ -82,6 +82,28 @@ int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D
                void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sattn_cached_mask - the full-attention slice mask that a dense iteration leaves for later ones.
+ *
+ * FG-Attn review, Figure 10 and its list of free parameters: every M x 1 slice (the `group`
+ * queries of a group against one key) that holds at least one full-attention softmax
+ * probability above tau_cached = 0.5 / N is kept, and the mask is reused by later iterations.
+ * With lse the natural-log row log-sum-exp of the dense pass (attn_forward's lse output):
+ *     keep (g, j)  <=>  max_{i in group g} exp(scale * Q[i].K[j] - lse[i]) >= tau
+ * (tau <= 0 keeps every key; a group may keep none).  Scores are bf16 x bf16 with fp32
+ * accumulation; the comparison is made in fp32.
+ *
+ *   q bf16 [B,H,Nq,D]; k bf16 [B,H,Nk,D]; lse fp32 [B,H,Nq] (caller-owned, device).
+ *   group: multiple of 16 in [16, 256]; D in {64, 128}; Nk <= SATTN_MASK_MAX_NK.
+ *   Outputs as sattn_mask: idx int32 [B,H,G,cap] ascending (entries past counts untouched),
+ *   counts int32 [B,H,G] = min(kept, cap); a list longer than cap keeps its first cap keys.
+ *   No workspace; nothing is allocated.
+ * Errors: SATTN_ERR_NULL, _SHAPE, _UNSUPPORTED, _ARG (cap < 1, scale, NaN tau, alignment), _HIP.
+ */
+int sattn_cached_mask(const void* q, const void* k, const float* lse,
+                      int B, int H, int Nq, int Nk, int D, int group, float tau, float scale,
+                      int32_t* idx, int32_t* counts, int cap, void* stream);
+
+/*
  * sattn_forward - fine-grained sparse attention forward over per-group key lists.
  *
  * FG-Attn review, "What carries the argument" and Fig. 6 / Fig. 7 captions: each group of

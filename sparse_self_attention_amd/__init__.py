@@ -8,6 +8,7 @@ missing or cannot be loaded, every call raises.
     idx, counts = mask(q, k, group=128, topk=k)            # or thresh=tau
     out, lse    = forward(q, k, v, idx, counts, group=128)
     out, lse    = attn(q, k, v)                            # dense control path
+    idx, counts = cached_mask(q, k, lse, group=128)        # slices with a probability >= 0.5/N
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["mask", "forward", "attn", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
+__all__ = ["mask", "forward", "attn", "cached_mask", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
            "library_path", "SattnError", "TOPK", "THRESH"]
 
 TOPK, THRESH = 0, 1
@@ -57,6 +58,8 @@ def _load():
     lib.sattn_forward.restype = I
     lib.attn_forward.argtypes = [P, P, P, I, I, I, I, I, F, P, I, P, P]
     lib.attn_forward.restype = I
+    lib.sattn_cached_mask.argtypes = [P, P, P, I, I, I, I, I, I, F, F, P, P, I, P]
+    lib.sattn_cached_mask.restype = I
     lib.sattn_voxel_permutation.argtypes = [I, I, I, I, I, I, P]
     lib.sattn_voxel_permutation.restype = I
     lib.sattn_permute_tokens.argtypes = [P, P, P, I, I, I, I, I, P]
@@ -173,6 +176,29 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[f
                           F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
     _check("attn_forward", st)
     return out, lse
+
+
+def cached_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int, *, tau: Optional[float] = None,
+                scale: Optional[float] = None, cap: Optional[int] = None, idx: Optional[torch.Tensor] = None,
+                counts: Optional[torch.Tensor] = None):
+    """Full-attention slice mask from a dense pass's lse (sattn_cached_mask); tau defaults to 0.5 / Nk."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
+    tau = 0.5 / Nk if tau is None else float(tau)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    G = -(-Nq // group)
+    if cap is None:
+        cap = Nk if idx is None else idx.shape[-1]
+    if idx is None:
+        idx = torch.empty((B, H, G, cap), dtype=torch.int32, device=q.device)
+    if counts is None:
+        counts = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    st = lib.sattn_cached_mask(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, D, group, tau, scale, _ptr(idx),
+                               _ptr(counts), idx.shape[-1], _stream_ptr(q))
+    _check("sattn_cached_mask", st)
+    return idx, counts
 
 
 def voxel_permutation(grid, voxel) -> torch.Tensor:

@@ -121,6 +121,25 @@ int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
 
+int sattn_cached_mask(const void* q, const void* k, const float* lse, int B, int H, int Nq, int Nk, int D,
+                      int group, float tau, float scale, int32_t* idx, int32_t* counts, int cap, void* stream) {
+  static const char* fn = "sattn_cached_mask";
+  if (!q || !k || !lse || !idx || !counts)
+    return fail(SATTN_ERR_NULL, "%s: q, k, lse, idx and counts must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
+  if (int r = check_group(fn, group)) return r;
+  if (int r = check_scale(fn, scale)) return r;
+  if (Nk > SATTN_MASK_MAX_NK) return fail(SATTN_ERR_UNSUPPORTED, "%s: Nk = %d > %d", fn, Nk, SATTN_MASK_MAX_NK);
+  if (tau != tau) return fail(SATTN_ERR_ARG, "%s: tau is NaN", fn);
+  if (cap < 1) return fail(SATTN_ERR_ARG, "%s: cap = %d must be >= 1", fn, cap);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4) || !aligned(idx, 4) || !aligned(counts, 4))
+    return fail(SATTN_ERR_ARG, "%s: q and k must be 16-byte aligned, lse, idx and counts 4-byte aligned", fn);
+  if ((int64_t)B * H * ((Nq + group - 1) / group) >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many groups", fn);
+  sattn::CachedMaskArgs a{q, k, lse, B, H, Nq, Nk, D, group, tau, scale, idx, counts, cap, stream};
+  const int err = sattn::launch_cached_mask(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
 int sattn_forward(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* counts, int cap,
                   int B, int H, int Nq, int Nk, int D, int group, float scale, void* out, int out_dtype, float* lse,
                   void* stream) {

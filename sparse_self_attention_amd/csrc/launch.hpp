@@ -50,6 +50,20 @@ int mask_heads_per_pass(int BH, int G, int Nk);
 size_t mask_workspace_bytes(int BH, int G, int Nk, int D);
 int launch_mask(const MaskArgs& a);
 
+struct CachedMaskArgs {
+  const void* q;
+  const void* k;
+  const float* lse;
+  int B, H, Nq, Nk, D, group;
+  float tau;
+  float scale;
+  int32_t* idx;
+  int32_t* counts;
+  int cap;
+  void* stream;
+};
+int launch_cached_mask(const CachedMaskArgs& a);
+
 int launch_permute_tokens(const void* src, void* dst, const int32_t* perm, int BH, int N, int D, int inverse,
                           void* stream);
 

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"sattn_mask", "sattn_forward", "attn_forward", "sattn_mask_workspace_bytes",
+    assert {"sattn_mask", "sattn_forward", "attn_forward", "sattn_mask_workspace_bytes", "sattn_cached_mask",
             "sattn_strerror", "sattn_last_error", "sattn_voxel_permutation", "sattn_permute_tokens"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sattn.h but not exported"
@@ -94,6 +94,25 @@ MASK_CASES = [
 @pytest.mark.parametrize("kw,code", MASK_CASES, ids=[str(c[0]) for c in MASK_CASES])
 def test_mask_validation(lib, kw, code):
     assert msk(lib, **kw) == code
+
+
+def cmk(lib, q=FAKE, k=FAKE, lse=FAKE, B=1, H=1, Nq=128, Nk=128, D=128, group=128, tau=0.01, scale=0.1,
+        idx=FAKE, counts=FAKE, cap=128):
+    return lib.sattn_cached_mask(q, k, lse, B, H, Nq, Nk, D, group, tau, scale, idx, counts, cap, P(0))
+
+
+CACHED_CASES = [
+    (dict(q=P(0)), ERR_NULL), (dict(lse=P(0)), ERR_NULL), (dict(idx=P(0)), ERR_NULL), (dict(counts=P(0)), ERR_NULL),
+    (dict(Nq=0), ERR_SHAPE), (dict(D=80), ERR_UNSUPPORTED), (dict(group=40), ERR_UNSUPPORTED),
+    (dict(Nk=200000), ERR_UNSUPPORTED), (dict(tau=float("nan")), ERR_ARG), (dict(cap=0), ERR_ARG),
+    (dict(scale=0.0), ERR_ARG), (dict(k=P(4104)), ERR_ARG), (dict(lse=P(4097)), ERR_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", CACHED_CASES, ids=[str(c[0]) for c in CACHED_CASES])
+def test_cached_mask_validation(lib, kw, code):
+    assert cmk(lib, **kw) == code
+    assert lib.sattn_last_error()
 
 
 def test_dense_validation(lib):
