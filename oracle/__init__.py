@@ -19,9 +19,12 @@ Readings of passages that the pages leave open:
   * top-k ties go to the lowest key index; index lists are ascending;
   * the cached mask keeps slice (g, j) when some query of group g gives key j a
     full-attention softmax probability of at least tau; tau <= 0 keeps every
-    key and a group may keep none.
+    key and a group may keep none;
+  * the Chipmunk sparse delta uses the full-softmax form the review asks for:
+    probabilities with a stale lse, no renormalisation over the selected keys.
 """
 from .attention import dense_attention_ref, sparse_attention_ref, sparse_attention_probs_ref  # noqa: F401
 from .mask import (group_mean_ref, group_scores_ref, topk_select_ref, thresh_select_ref,  # noqa: F401
                    mask_ref)
-from .cached import row_lse_ref, slice_max_logprob_ref, cached_mask_ref  # noqa: F401
+from .cached import (row_lse_ref, slice_max_logprob_ref, cached_mask_ref, colsum_scores_ref,  # noqa: F401
+                     colsum_mask_ref, delta_fresh_ref, delta_forward_ref)

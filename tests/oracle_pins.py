@@ -363,3 +363,94 @@ def check_cached_properties(cached, row_lse):
     lse = row_lse(q, k, scale)
     assert _kept_sets(cached(q, k, M, 0.03, scale, lse=lse)) == _kept_sets(cached(q, k, M, 0.03, scale))
     assert G * M == Nq
+
+
+# ----------------------------------------------------------------------------
+# Chipmunk sparse deltas: column sums and the cached-output update
+# ----------------------------------------------------------------------------
+
+def check_colsum(colsum_scores, colsum_mask, row_lse):
+    """Column sums against explicit loops, against softmax rows summing to 1, against single-query
+    groups; top-k of the column sums by brute-force rank counting with ties to the lower index."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(31)
+    B, H, Nq, Nk, D, M = 1, 2, 12, 15, 4, 4
+    q, k, _ = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=2.0)
+    scale = 1.0 / math.sqrt(D)
+    lse = row_lse(q, k, scale)
+    cs = colsum_scores(q, k, M, scale, lse)
+    for (b, h, g), row in cs.items():
+        for j in range(Nk):
+            want = 0.0
+            for i in range(g * M, min((g + 1) * M, Nq)):
+                s = math.fsum(float(q[b, h, i, d]) * float(k[b, h, j, d]) for d in range(D)) * scale
+                want += math.exp(s - float(lse[b, h, i]))
+            assert abs(row[j] - want) <= 1e-12 * max(1.0, want)
+        rows = min((g + 1) * M, Nq) - g * M
+        assert abs(row.sum() - rows) <= 1e-12 * rows
+    s = np.einsum("bhid,bhjd->bhij", q, k) * scale
+    one = colsum_scores(q, k, 1, scale, lse)
+    p = softmax(s, axis=-1)
+    for (b, h, i), row in one.items():
+        assert np.allclose(row, p[b, h, i], rtol=0, atol=1e-14)
+    # top-k by rank counting; duplicate key rows create exact ties
+    k2 = k.copy()
+    k2[:, :, 7] = k2[:, :, 3]
+    k2[:, :, 11] = k2[:, :, 3]
+    lse2 = row_lse(q, k2, scale)
+    cs2 = colsum_scores(q, k2, M, scale, lse2)
+    for topk in (1, 4, 8, 15):
+        res = colsum_mask(q, k2, M, topk, scale, lse2)
+        for (b, h, g), row in cs2.items():
+            lst = res["idx"][b, h, g, :res["counts"][b, h, g]]
+            assert res["counts"][b, h, g] == topk and np.all(np.diff(lst) > 0)
+            for j in range(Nk):
+                rank = sum(1 for jj in range(Nk) if row[jj] > row[j] or (row[jj] == row[j] and jj < j))
+                assert (j in lst) == (rank < topk), (topk, j, rank)
+
+
+def check_delta(delta_fresh, delta_forward):
+    """Every key with the exact lse gives dense attention (torch SDPA); one key gives exp(s - lse) v;
+    an unchanged step leaves the cached output untouched; linear in V; lse shift scales by e^-c."""
+    import torch
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(37)
+    B, H, Nq, Nk, D, M = 1, 2, 20, 17, 8, 8
+    q, k, v = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=2.0)
+    scale = 1.0 / math.sqrt(D)
+    G = -(-Nq // M)
+    s = np.einsum("bhid,bhjd->bhij", q, k) * scale
+    lse = logsumexp(s, axis=-1)
+    idx_all = np.broadcast_to(np.arange(Nk, dtype=np.int32), (B, H, G, Nk)).copy()
+    cnt_all = np.full((B, H, G), Nk, dtype=np.int32)
+    fresh = delta_fresh(q, k, v, idx_all, cnt_all, M, scale, lse)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=scale).numpy()
+    assert np.allclose(fresh, ref, rtol=0, atol=1e-12)
+    # one listed key per group: fresh_i = exp(s_ij - lse_i) v_j
+    idx1 = np.full((B, H, G, 1), 5, dtype=np.int32)
+    idx1[0, 1, 1, 0] = 12
+    cnt1 = np.ones((B, H, G), dtype=np.int32)
+    f1 = delta_fresh(q, k, v, idx1, cnt1, M, scale, lse)
+    for h in range(H):
+        for i in range(Nq):
+            j = int(idx1[0, h, i // M, 0])
+            assert np.allclose(f1[0, h, i], math.exp(s[0, h, i, j] - lse[0, h, i]) * v[0, h, j], rtol=0, atol=1e-12)
+    # random subsets: unchanged inputs leave the cached output untouched; linearity; lse shift
+    idx, counts = _random_lists(rng, B, H, G, Nk, 9)
+    f = delta_fresh(q, k, v, idx, counts, M, scale, lse)
+    out_prev = rng.standard_normal((B, H, Nq, D))
+    out, f_new = delta_forward(q, k, v, idx, counts, M, scale, lse, out_prev, f)
+    assert np.allclose(out, out_prev, rtol=0, atol=1e-12) and np.allclose(f_new, f, rtol=0, atol=0)
+    out2, _ = delta_forward(q, k, v, idx, counts, M, scale, lse, out_prev, np.zeros_like(f))
+    assert np.allclose(out2, out_prev + f, rtol=0, atol=1e-12)
+    v2 = rng.standard_normal(v.shape)
+    lin = delta_fresh(q, k, v + 2.0 * v2, idx, counts, M, scale, lse)
+    assert np.allclose(lin, f + 2.0 * delta_fresh(q, k, v2, idx, counts, M, scale, lse), rtol=0, atol=1e-11)
+    shifted = delta_fresh(q, k, v, idx, counts, M, scale, lse + 0.7)
+    assert np.allclose(shifted, f * math.exp(-0.7), rtol=0, atol=1e-12)
+    # an empty list contributes nothing
+    c0 = counts.copy()
+    c0[0, 0, 0] = 0
+    f0 = delta_fresh(q, k, v, idx, c0, M, scale, lse)
+    assert np.all(f0[0, 0, :M] == 0.0)

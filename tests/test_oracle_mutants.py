@@ -84,6 +84,33 @@ CACHED_MUTANTS = [
 ]
 
 
+DELTA_MUTANTS = [
+    ("column max instead of sum", "out[(b, h, g)] = np.exp(s - lse[b, h, r0:r1, None]).sum(axis=0)",
+     "out[(b, h, g)] = np.exp(s - lse[b, h, r0:r1, None]).max(axis=0)"),
+    ("column sums without lse", "out[(b, h, g)] = np.exp(s - lse[b, h, r0:r1, None]).sum(axis=0)",
+     "out[(b, h, g)] = np.exp(s).sum(axis=0)"),
+    ("column sums over the wrong rows", "r0, r1 = g * group, min((g + 1) * group, Nq)\n        s = np.matmul(q[b, h, r0:r1], k[b, h].T) * scale\n        out[(b, h, g)] = np.exp(",
+     "r0, r1 = g * group, min((g + 1) * group + 1, Nq)\n        s = np.matmul(q[b, h, r0:r1], k[b, h].T) * scale\n        out[(b, h, g)] = np.exp("),
+    ("top-k ties to the higher index", "order = np.lexsort((np.arange(Nk), -row))", "order = np.lexsort((-np.arange(Nk), -row))"),
+    ("top-k keeps the smallest sums", "order = np.lexsort((np.arange(Nk), -row))", "order = np.lexsort((np.arange(Nk), row))"),
+    ("restricted softmax (renormalised)", "fresh[b, h, r0:r1] = np.matmul(np.exp(s - lse[b, h, r0:r1, None]), v[b, h, J])",
+     "e = np.exp(s - lse[b, h, r0:r1, None]); fresh[b, h, r0:r1] = np.matmul(e / e.sum(axis=1, keepdims=True), v[b, h, J])"),
+    ("stale part added", "out = np.asarray(out_prev, dtype=np.float64) - np.asarray(fresh_prev, dtype=np.float64) + fresh",
+     "out = np.asarray(out_prev, dtype=np.float64) + np.asarray(fresh_prev, dtype=np.float64) - fresh"),
+    ("delta without lse", "np.exp(s - lse[b, h, r0:r1, None]), v[b, h, J]", "np.exp(s), v[b, h, J]"),
+    ("V rows not gathered", "v[b, h, J])", "v[b, h, :J.size])"),
+    ("delta scale dropped", "s = np.matmul(q[b, h, r0:r1], k[b, h, J].T) * scale", "s = np.matmul(q[b, h, r0:r1], k[b, h, J].T)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", DELTA_MUTANTS, ids=[m[0] for m in DELTA_MUTANTS])
+def test_delta_mutant_is_caught(name, old, new):
+    m = _mutant("oracle.cached", old, new)
+    checks = [lambda: pins.check_colsum(m.colsum_scores_ref, m.colsum_mask_ref, m.row_lse_ref),
+              lambda: pins.check_delta(m.delta_fresh_ref, m.delta_forward_ref)]
+    assert _caught(checks), f"no pin catches the planted mistake: {name}"
+
+
 @pytest.mark.parametrize("name,old,new", CACHED_MUTANTS, ids=[m[0] for m in CACHED_MUTANTS])
 def test_cached_mutant_is_caught(name, old, new):
     m = _mutant("oracle.cached", old, new)
