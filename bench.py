@@ -278,6 +278,27 @@ def main():
                               "density": round(tot / (w.heads * G * w.n_k), 4),
                               "pooled_topk_recall": round(hit / max(tot, 1), 4)}
         del cidx, ccnt
+        # Chipmunk sparse deltas on the same step: column-sum top-k lists from the dense lse, then one
+        # delta step (stale lse, cached output and fresh part in fp32)
+        def timed(fn, n=3):
+            ts = []
+            for _ in range(n):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return float(np.median(ts))
+        cs_ms = timed(lambda: sattn.colsum_mask(q0, k0, lse, w.group, w.topk, idx=idx, counts=counts, workspace=ws))
+        out_prev = torch.zeros(q0.shape, dtype=torch.float32, device=dev)
+        fresh = torch.zeros_like(out_prev)
+        dout = torch.empty_like(out_prev)
+        d_ms = timed(lambda: sattn.delta_forward(qs[-1], ks[-1], v, idx, counts, w.group, lse=lse, out_prev=out_prev,
+                                                 fresh=fresh, out=dout))
+        rec["chipmunk_delta"] = {"colsum_mask_ms": round(cs_ms, 3), "delta_fwd_ms": round(d_ms, 3),
+                                 "delta_kept_tflops": round(kflops / (d_ms * 1e-3) / 1e12, 2)}
+        del out_prev, fresh, dout
     if not args.no_cpu_baseline and not args.kernel_only:
         # oracle on the step-0 inputs with the step-0 lists
         sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)

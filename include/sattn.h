@@ -82,6 +82,26 @@ int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D
                void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sattn_colsum_mask - Chipmunk's selection: per group, the topk keys with the largest column sums
+ * of attention probabilities.
+ *
+ * Chipmunk review, Referee major comment 2 (Alg. 4 and Appendix B.2): a chunk's columns are
+ * ranked by the summed attention probabilities of its queries, computed with the softmax
+ * normalisation constants of an earlier step, and the top-k indices are cached for the sparse
+ * steps.  With lse the natural-log row log-sum-exp of that step (attn_forward's lse):
+ *     c[g][j] = sum_{i in group g} exp(scale * Q[i].K[j] - lse[i]),   keep the topk largest
+ * (ties to the lowest key index; lists ascending, counts = topk).  bf16 inputs, fp32 sums.
+ *
+ *   q, k, group, topk, scale, idx, counts, cap, workspace, ws_bytes: as sattn_mask in top-k mode
+ *   (the workspace size is sattn_mask_workspace_bytes()).  lse fp32 [B,H,Nq] (device).
+ * Errors: as sattn_mask.
+ */
+int sattn_colsum_mask(const void* q, const void* k, const float* lse,
+                      int B, int H, int Nq, int Nk, int D, int group, int topk, float scale,
+                      int32_t* idx, int32_t* counts, int cap,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * sattn_cached_mask - the full-attention slice mask that a dense iteration leaves for later ones.
  *
  * FG-Attn review, Figure 10 and its list of free parameters: every M x 1 slice (the `group`
@@ -129,6 +149,31 @@ int sattn_forward(const void* q, const void* k, const void* v,
                   const int32_t* idx, const int32_t* counts, int cap,
                   int B, int H, int Nq, int Nk, int D, int group, float scale,
                   void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * sattn_delta_forward - Chipmunk sparse-delta step: refresh only the listed keys' part of a
+ * cached attention output.
+ *
+ * Chipmunk review, "What carries the argument" and Referee major comments 1-2: the output of
+ * a step is the cached output plus a sparse correction recomputed for the selected columns of
+ * K^T and rows of V, with the softmax normalisation constants of an earlier step reused.  In
+ * the full-softmax form the review asks for, with a stale lse and kept keys J of group g:
+ *     fresh_new[i] = sum_{j in J} exp(scale * Q[i].K[j] - lse[i]) V[j]     (no renormalisation)
+ *     out[i]       = out_prev[i] - fresh[i] + fresh_new[i],   then fresh[i] <- fresh_new[i].
+ * At a dense step the caller keeps the dense output as out_prev and obtains the first fresh
+ * part by one call with out_prev = fresh = 0.
+ *
+ *   q, k, v, idx, counts, cap, group, scale: as sattn_forward (same list preconditions).
+ *   lse      fp32 [B,H,Nq], natural log (e.g. attn_forward's lse of the dense step).
+ *   out_prev fp32 [B,H,Nq,D] cached output; fresh fp32 [B,H,Nq,D] in: previous part, out: new part.
+ *   out      [B,H,Nq,D] bf16 or fp32 per out_dtype; may be out_prev itself when fp32 (in place).
+ * Errors: as sattn_forward.
+ */
+int sattn_delta_forward(const void* q, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* counts, int cap,
+                        int B, int H, int Nq, int Nk, int D, int group, float scale,
+                        const float* lse, const float* out_prev, float* fresh,
+                        void* out, int out_dtype, void* stream);
 
 /*
  * attn_forward - dense control path: every query attends to every key.

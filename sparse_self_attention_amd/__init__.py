@@ -9,6 +9,8 @@ missing or cannot be loaded, every call raises.
     out, lse    = forward(q, k, v, idx, counts, group=128)
     out, lse    = attn(q, k, v)                            # dense control path
     idx, counts = cached_mask(q, k, lse, group=128)        # slices with a probability >= 0.5/N
+    idx, counts = colsum_mask(q, k, lse, group=192, topk=k)  # Chipmunk column-sum selection
+    out = delta_forward(q, k, v, idx, counts, 192, lse=lse, out_prev=out, fresh=fresh)  # sparse delta
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["mask", "forward", "attn", "cached_mask", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
+__all__ = ["mask", "forward", "attn", "cached_mask", "colsum_mask", "delta_forward", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
            "library_path", "SattnError", "TOPK", "THRESH"]
 
 TOPK, THRESH = 0, 1
@@ -60,6 +62,10 @@ def _load():
     lib.attn_forward.restype = I
     lib.sattn_cached_mask.argtypes = [P, P, P, I, I, I, I, I, I, F, F, P, P, I, P]
     lib.sattn_cached_mask.restype = I
+    lib.sattn_colsum_mask.argtypes = [P, P, P, I, I, I, I, I, I, I, F, P, P, I, P, Z, P]
+    lib.sattn_colsum_mask.restype = I
+    lib.sattn_delta_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, P, I, P]
+    lib.sattn_delta_forward.restype = I
     lib.sattn_voxel_permutation.argtypes = [I, I, I, I, I, I, P]
     lib.sattn_voxel_permutation.restype = I
     lib.sattn_permute_tokens.argtypes = [P, P, P, I, I, I, I, I, P]
@@ -102,6 +108,11 @@ def _check_qkv(q, k, v=None):
     if v is not None and v.shape != k.shape:
         raise ValueError("v must have the shape of k")
     return B, H, Nq, k.shape[2], D
+
+
+def _check_lse(lse, B, H, Nq):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
 
 
 def mask_workspace_bytes(B: int, H: int, Nq: int, Nk: int, D: int, group: int) -> int:
@@ -184,8 +195,7 @@ def cached_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int,
     """Full-attention slice mask from a dense pass's lse (sattn_cached_mask); tau defaults to 0.5 / Nk."""
     lib = _load()
     B, H, Nq, Nk, D = _check_qkv(q, k)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
+    _check_lse(lse, B, H, Nq)
     tau = 0.5 / Nk if tau is None else float(tau)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     G = -(-Nq // group)
@@ -199,6 +209,58 @@ def cached_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int,
                                _ptr(counts), idx.shape[-1], _stream_ptr(q))
     _check("sattn_cached_mask", st)
     return idx, counts
+
+
+def colsum_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int, topk: int, *,
+                scale: Optional[float] = None, cap: Optional[int] = None, idx: Optional[torch.Tensor] = None,
+                counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Top-k keys per group by column sums of attention probabilities with a given lse (sattn_colsum_mask)."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k)
+    _check_lse(lse, B, H, Nq)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    G = -(-Nq // group)
+    if cap is None:
+        cap = int(topk) if idx is None else idx.shape[-1]
+    if idx is None:
+        idx = torch.empty((B, H, G, cap), dtype=torch.int32, device=q.device)
+    if counts is None:
+        counts = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    need = lib.sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.sattn_colsum_mask(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, D, group, int(topk), scale, _ptr(idx),
+                               _ptr(counts), idx.shape[-1], _ptr(workspace), workspace.numel(), _stream_ptr(q))
+    _check("sattn_colsum_mask", st)
+    return idx, counts
+
+
+def delta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, counts: torch.Tensor,
+                  group: int, *, lse: torch.Tensor, out_prev: torch.Tensor, fresh: torch.Tensor,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  out_dtype: torch.dtype = torch.float32):
+    """Chipmunk sparse-delta step (sattn_delta_forward): returns out; updates fresh in place."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k, v)
+    G = -(-Nq // group)
+    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
+        raise ValueError("idx and counts must be contiguous int32")
+    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
+        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    _check_lse(lse, B, H, Nq)
+    for name, t in (("out_prev", out_prev), ("fresh", fresh)):
+        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor shaped like q")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or fp32 tensor shaped like q")
+    st = lib.sattn_delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk,
+                                 D, group, scale, _ptr(lse), _ptr(out_prev), _ptr(fresh), _ptr(out),
+                                 F32 if out.dtype == torch.float32 else BF16, _stream_ptr(q))
+    _check("sattn_delta_forward", st)
+    return out
 
 
 def voxel_permutation(grid, voxel) -> torch.Tensor:

@@ -121,6 +121,29 @@ int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
 
+int sattn_colsum_mask(const void* q, const void* k, const float* lse, int B, int H, int Nq, int Nk, int D,
+                      int group, int topk, float scale, int32_t* idx, int32_t* counts, int cap, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  static const char* fn = "sattn_colsum_mask";
+  if (!q || !k || !lse || !idx || !counts)
+    return fail(SATTN_ERR_NULL, "%s: q, k, lse, idx and counts must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
+  if (int r = check_group(fn, group)) return r;
+  if (int r = check_scale(fn, scale)) return r;
+  if (Nk > SATTN_MASK_MAX_NK) return fail(SATTN_ERR_UNSUPPORTED, "%s: Nk = %d > %d", fn, Nk, SATTN_MASK_MAX_NK);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4) || !aligned(idx, 4) || !aligned(counts, 4))
+    return fail(SATTN_ERR_ARG, "%s: q and k must be 16-byte aligned, lse, idx and counts 4-byte aligned", fn);
+  if (topk < 1 || topk > Nk) return fail(SATTN_ERR_ARG, "%s: topk = %d not in [1, Nk = %d]", fn, topk, Nk);
+  if (cap < topk) return fail(SATTN_ERR_ARG, "%s: cap = %d < topk = %d", fn, cap, topk);
+  const size_t need = sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(SATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-byte aligned), got %zu", fn, need, ws_bytes);
+  sattn::MaskArgs a{q, k, B, H, Nq, Nk, D, group, 2, topk, 0.0f, scale, idx, counts, cap, workspace, ws_bytes, stream};
+  a.lse = lse;
+  const int err = sattn::launch_mask(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
 int sattn_cached_mask(const void* q, const void* k, const float* lse, int B, int H, int Nq, int Nk, int D,
                       int group, float tau, float scale, int32_t* idx, int32_t* counts, int cap, void* stream) {
   static const char* fn = "sattn_cached_mask";
@@ -166,6 +189,39 @@ int sattn_forward(const void* q, const void* k, const void* v, const int32_t* id
   }
   sattn::FwdArgs a{q, k, v, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out, out_dtype == SATTN_F32, lse,
                    false, stream};
+  const int err = sattn::launch_attn_fwd(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
+int sattn_delta_forward(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* counts,
+                        int cap, int B, int H, int Nq, int Nk, int D, int group, float scale, const float* lse,
+                        const float* out_prev, float* fresh, void* out, int out_dtype, void* stream) {
+  static const char* fn = "sattn_delta_forward";
+  if (!q || !k || !v || !idx || !counts || !lse || !out_prev || !fresh || !out)
+    return fail(SATTN_ERR_NULL, "%s: q, k, v, idx, counts, lse, out_prev, fresh and out must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
+  if (int r = check_group(fn, group)) return r;
+  if (int r = check_scale(fn, scale)) return r;
+  if (cap < 1) return fail(SATTN_ERR_ARG, "%s: cap = %d must be >= 1", fn, cap);
+  if (out_dtype != SATTN_BF16 && out_dtype != SATTN_F32) return fail(SATTN_ERR_ARG, "%s: bad out_dtype", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(out_prev, 16) ||
+      !aligned(fresh, 16) || !aligned(idx, 4) || !aligned(counts, 4) || !aligned(lse, 4))
+    return fail(SATTN_ERR_ARG, "%s: q, k, v, out, out_prev, fresh must be 16-byte aligned; idx, counts, lse 4-byte",
+                fn);
+  const int64_t G = (Nq + group - 1) / group;
+  if ((int64_t)B * H * G >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many groups", fn);
+  if (validate_mode()) {
+    int flag = 0;
+    const int err = sattn::validate_index_lists(idx, counts, cap, (int)(B * H * G), Nk, stream, &flag);
+    if (err) return hip_fail(err, fn);
+    if (flag) return fail(SATTN_ERR_INDEX, "%s: index lists invalid (code %d)", fn, flag);
+  }
+  sattn::FwdArgs a{q, k, v, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out, out_dtype == SATTN_F32, nullptr,
+                   false, stream};
+  a.delta = true;
+  a.lse_in = lse;
+  a.out_prev = out_prev;
+  a.fresh = fresh;
   const int err = sattn::launch_attn_fwd(a);
   return err ? hip_fail(err, fn) : SATTN_OK;
 }

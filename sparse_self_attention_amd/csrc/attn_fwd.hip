@@ -65,12 +65,16 @@ using IC = std::integral_constant<int, N>;
 // interleave MFMA and softmax work of different waves.
 constexpr int BKL = 32;
 
-template <int D, int NW, bool DENSE, bool OUT_F32>
+// DELTA: the Chipmunk sparse-delta update instead of the softmax.  The probabilities use the given
+// (stale) lse instead of a running max and are not renormalised; the epilogue forms
+// out = out_prev - fresh + sum_j p_j v_j and stores the new sum into fresh.
+template <int D, int NW, bool DENSE, bool OUT_F32, bool DELTA>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_lean(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap,
     int Nq, int Nk, int group, int G, float scale_log2, void* __restrict__ out, float* __restrict__ lse,
-    uint32_t n_units) {
+    uint32_t n_units, const float* __restrict__ lse_in, const float* __restrict__ out_prev,
+    float* __restrict__ fresh) {
   using L = FwdLayout<D, BKL>;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_BYTES];
@@ -152,6 +156,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 #pragma unroll
   for (int i = 0; i < L::DBLK; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
+  if (DELTA) m_run = row_valid ? lse_in[(size_t)bh * Nq + r0 + wrow] * 1.4426950408889634f : 0.0f;
 
   auto block = [&](auto st, int j) {
     constexpr int ST = decltype(st)::value;
@@ -201,9 +206,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
         lsum += p0 + p1;   // plain fp32 adds: a dot2 row sum would stall on the running MFMAs
       }
     };
-    if (j == 0) take_max();
+    if (!DELTA && j == 0) take_max();
     exps();
-    if (__builtin_amdgcn_ballot_w64(!(lsum <= 0x1p64f)) != 0) {   // also true for inf / nan
+    if (!DELTA && __builtin_amdgcn_ballot_w64(!(lsum <= 0x1p64f)) != 0) {   // also true for inf / nan
       take_max();
       exps();
     }
@@ -237,6 +242,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   }
   if (j < nblk) block(IC<0>{}, j);
 
+  if constexpr (DELTA) {
+    if (row_valid) {
+      const size_t orow = ((size_t)bh * Nq + r0 + wrow) * D;
+#pragma unroll
+      for (int db = 0; db < L::DBLK; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 32 * db + 8 * i + 4 * hi;
+          const f32x4 fo = *(const f32x4*)(fresh + orow + d0);
+          const f32x4 op = *(const f32x4*)(out_prev + orow + d0);
+          const f32x4 fn = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+          const f32x4 x = op - fo + fn;
+          *(f32x4*)(fresh + orow + d0) = fn;
+          if (OUT_F32) *(f32x4*)((float*)out + orow + d0) = x;
+          else *(u32x2*)((uint16_t*)out + orow + d0) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        }
+    }
+    return;
+  }
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_valid) {
@@ -256,31 +280,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   }
 }
 
-template <int D, int NW, bool DENSE>
+template <int D, int NW, bool DENSE, bool DELTA>
 static int launch_lean_t(const FwdArgs& a) {
   const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
   const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)a.stream;
   if (a.out_f32)
-    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true>), dim3(n_units), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
-                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
+                       a.fresh);
   else
-    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false>), dim3(n_units), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
-                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
+                       a.fresh);
   return (int)hipGetLastError();
+}
+
+template <int D, bool DELTA>
+static int launch_sparse_d(const FwdArgs& a) {
+  const int waves = (a.group + 31) / 32;
+  if (waves <= 2) return launch_lean_t<D, 2, false, DELTA>(a);
+  if (waves <= 4) return launch_lean_t<D, 4, false, DELTA>(a);
+  if (waves <= 6) return launch_lean_t<D, 6, false, DELTA>(a);
+  return launch_lean_t<D, 8, false, DELTA>(a);
 }
 
 template <int D>
 static int launch_fwd_d(const FwdArgs& a) {
-  if (a.dense) return launch_lean_t<D, 4, true>(a);
-  const int waves = (a.group + 31) / 32;
-  if (waves <= 2) return launch_lean_t<D, 2, false>(a);
-  if (waves <= 4) return launch_lean_t<D, 4, false>(a);
-  if (waves <= 6) return launch_lean_t<D, 6, false>(a);
-  return launch_lean_t<D, 8, false>(a);
+  if (a.dense) return launch_lean_t<D, 4, true, false>(a);
+  return a.delta ? launch_sparse_d<D, true>(a) : launch_sparse_d<D, false>(a);
 }
 
 int launch_attn_fwd(const FwdArgs& a) {

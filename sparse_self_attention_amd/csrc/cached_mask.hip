@@ -24,11 +24,18 @@
 //  * Each wave ballots "max x >= log2 tau" for the block's 32 keys and ORs the word into an LDS
 //    bitmap of the group's keys; at the end the workgroup writes the ascending list from the
 //    bitmap (popcounts, one block scan, then each thread emits the set bits of its words in order).
+//
+// The same walk also gives the column sums of Chipmunk's selection (Chipmunk review, Referee major
+// comment 2: Alg. 4 ranks the columns of a chunk by their summed attention probabilities, with
+// the normalisation constants of an earlier step): COLSUM = true sums exp2(x) over the group's
+// rows instead of taking the max (in-lane sum, lane-pair sum, then the waves' partials in a fixed
+// order) and stores the fp32 sums in the staging layout that the top-k selection reads.
 #include <math.h>
 
 #include "../../include/sattn.h"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "stage_layout.hpp"
 
 namespace sattn {
 
@@ -75,24 +82,26 @@ __device__ inline int wg_excl_scan(int x, int* wsum, int& total) {
 
 }  // namespace
 
-// Dynamic LDS: the group's key bitmap, ceil(Nk / 32) words.
-template <int D, int NW>
+// Dynamic LDS: the group's key bitmap, ceil(Nk / 32) words (none for COLSUM).
+template <int D, int NW, bool COLSUM>
 __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const float* __restrict__ lse, int Nq, int Nk,
                                                           int group, int G, float scale_log2, float log2_tau,
                                                           int32_t* __restrict__ idx, int32_t* __restrict__ counts,
-                                                          int cap, uint32_t n_units) {
+                                                          int cap, uint32_t n_units, float* __restrict__ csum,
+                                                          float* __restrict__ csamp, int bh0) {
   using L = CmLayout<D>;
   constexpr int NT = NW * 64;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   __shared__ __attribute__((aligned(1024))) char stage[2 * L::STAGE_BYTES];
   __shared__ int wsum[NW];
+  __shared__ float part[COLSUM ? 2 : 1][NW][32];
   extern __shared__ uint32_t bm[];
 
   const uint32_t unit = xcd_contiguous(blockIdx.x, n_units);
   const int g = (int)(unit % (uint32_t)G);
-  const uint32_t bh = unit / (uint32_t)G;
+  const uint32_t bh = unit / (uint32_t)G + (uint32_t)bh0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,7 +111,23 @@ __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restr
   const int nwords = (Nk + 31) / 32;
   const int nblk = nwords;
 
-  for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
+  if (!COLSUM)
+    for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
+  // COLSUM: the column sums of block blk, summed over the waves in order, to the staging rows
+  float* crow = COLSUM ? csum + (size_t)unit * score_stride(Nk) : nullptr;
+  float* srow = COLSUM ? csamp + (size_t)unit * sample_stride(Nk) : nullptr;
+  auto flush = [&](int blk) {
+    if (wave == 0 && lane < 32) {
+      const int key = blk * CM_BK + lane;
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += part[blk & 1][w][lane];
+      if (key < Nk) {
+        crow[key] = t;
+        if (key % SAMPLE_STEP == 0) srow[key / SAMPLE_STEP] = t;
+      }
+    }
+  };
 
   // A operand: this lane's query row ql of the wave, chunk (2 ks + hi); rows outside the group read 0
   bf16x8 qf[L::KSTEPS];
@@ -153,6 +178,7 @@ __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restr
     wait_vmcnt0();
     __syncthreads();   // stage j landed for every wave; stage j+1 is free again
     if (j + 1 < nblk) issue(stage + (1 - st) * L::STAGE_BYTES, j + 1);
+    if (COLSUM && j > 0) flush(j - 1);   // every wave's partial of block j-1 is in LDS
     const char* sk = stage + st * L::STAGE_BYTES;
     f32x16 acc = {};
 #pragma unroll
@@ -160,15 +186,27 @@ __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restr
       const bf16x8 b = *(const bf16x8*)(sk + koff[ks]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], b, acc, 0, 0, 0);
     }
-    float mx = __builtin_fmaf(acc[0], scale_log2, -lrow[0]);
+    if constexpr (COLSUM) {
+      float ps = 0.0f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, __builtin_fmaf(acc[r], scale_log2, -lrow[r]));
-    mx = pair_max(mx);
-    const bool valid = j * CM_BK + ql < Nk;
-    const uint64_t keep = __builtin_amdgcn_ballot_w64(valid && mx >= log2_tau);
-    if (lane == 0 && (uint32_t)keep != 0u) atomicOr(&bm[j], (uint32_t)keep);
+      for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], scale_log2, -lrow[r]));
+      ps = pair_sum(ps);
+      if (lane < 32) part[st][wave][lane] = ps;
+    } else {
+      float mx = __builtin_fmaf(acc[0], scale_log2, -lrow[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, __builtin_fmaf(acc[r], scale_log2, -lrow[r]));
+      mx = pair_max(mx);
+      const bool valid = j * CM_BK + ql < Nk;
+      const uint64_t keep = __builtin_amdgcn_ballot_w64(valid && mx >= log2_tau);
+      if (lane == 0 && (uint32_t)keep != 0u) atomicOr(&bm[j], (uint32_t)keep);
+    }
   }
   __syncthreads();
+  if constexpr (COLSUM) {
+    flush(nblk - 1);
+    return;
+  }
 
   // ascending list: each thread owns a contiguous run of words
   const int per = (nwords + NT - 1) / NT;
@@ -196,9 +234,9 @@ static int launch_cached_t(const CachedMaskArgs& a) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   const float log2_tau = a.tau > 0.0f ? log2f(a.tau) : -INFINITY;
   const size_t lds = (size_t)((a.Nk + 31) / 32) * 4;   // at most 16 KB (Nk <= 131072)
-  hipLaunchKernelGGL((k_cached_mask<D, NW>), dim3(n_units), dim3(NW * 64), lds, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((k_cached_mask<D, NW, false>), dim3(n_units), dim3(NW * 64), lds, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, a.lse, a.Nq, a.Nk, a.group, (int)G, scale_log2,
-                     log2_tau, a.idx, a.counts, a.cap, n_units);
+                     log2_tau, a.idx, a.counts, a.cap, n_units, nullptr, nullptr, 0);
   return (int)hipGetLastError();
 }
 
@@ -213,6 +251,30 @@ static int launch_cached_d(const CachedMaskArgs& a) {
 
 int launch_cached_mask(const CachedMaskArgs& a) {
   return a.D == 64 ? launch_cached_d<64>(a) : launch_cached_d<128>(a);
+}
+
+template <int D, int NW>
+static int launch_colsum_t(const ColsumArgs& a) {
+  const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
+  const uint32_t n_units = (uint32_t)a.nheads * G;
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((k_cached_mask<D, NW, true>), dim3(n_units), dim3(NW * 64), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, a.lse, a.Nq, a.Nk, a.group, (int)G, scale_log2,
+                     0.0f, nullptr, nullptr, 1, n_units, a.scores, a.samples, a.bh0);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+static int launch_colsum_d(const ColsumArgs& a) {
+  const int waves = (a.group + 31) / 32;
+  if (waves <= 2) return launch_colsum_t<D, 2>(a);
+  if (waves <= 4) return launch_colsum_t<D, 4>(a);
+  if (waves <= 6) return launch_colsum_t<D, 6>(a);
+  return launch_colsum_t<D, 8>(a);
+}
+
+int launch_colsum_scores(const ColsumArgs& a) {
+  return a.D == 64 ? launch_colsum_d<64>(a) : launch_colsum_d<128>(a);
 }
 
 }  // namespace sattn

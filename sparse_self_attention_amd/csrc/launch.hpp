@@ -22,6 +22,11 @@ struct FwdArgs {
   float* lse;
   bool dense;
   void* stream;
+  // sparse-delta update (sattn_delta_forward): stale lse, cached output, running fresh part
+  bool delta = false;
+  const float* lse_in = nullptr;
+  const float* out_prev = nullptr;
+  float* fresh = nullptr;
 };
 int launch_attn_fwd(const FwdArgs& a);
 
@@ -34,7 +39,7 @@ struct MaskArgs {
   const void* q;
   const void* k;
   int B, H, Nq, Nk, D, group;
-  int mode;        // 0 top-k, 1 threshold
+  int mode;        // 0 top-k, 1 threshold (both on the group-mean scores), 2 top-k of column sums
   int topk;
   float thresh;
   float scale;
@@ -44,6 +49,7 @@ struct MaskArgs {
   void* workspace;
   size_t ws_bytes;
   void* stream;
+  const float* lse = nullptr;   // mode 2: row lse of the step whose normalisation is reused
 };
 // Number of (batch, head) pairs whose scores are held in the workspace at once.
 int mask_heads_per_pass(int BH, int G, int Nk);
@@ -63,6 +69,21 @@ struct CachedMaskArgs {
   void* stream;
 };
 int launch_cached_mask(const CachedMaskArgs& a);
+
+// Column sums of attention probabilities with a given lse, c[g][j] = sum_{i in g} exp(scale q_i.k_j - lse_i),
+// for heads [bh0, bh0 + nheads), written in the staging layout of stage_layout.hpp (rows and samples).
+struct ColsumArgs {
+  const void* q;
+  const void* k;
+  const float* lse;
+  int Nq, Nk, D, group;
+  float scale;
+  float* scores;
+  float* samples;
+  int bh0, nheads;
+  void* stream;
+};
+int launch_colsum_scores(const ColsumArgs& a);
 
 int launch_permute_tokens(const void* src, void* dst, const int32_t* perm, int BH, int N, int D, int inverse,
                           void* stream);

@@ -26,20 +26,13 @@
 #include "../../include/sattn.h"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "stage_layout.hpp"
 
 namespace sattn {
 
 constexpr size_t SCORE_STAGE_BUDGET = 1024ull << 20;  // bytes of fp32 scores staged per pass
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-// fp32 score rows are padded to a multiple of 4 floats so 16-byte stores stay aligned
-static inline __host__ __device__ int score_stride(int Nk) { return (Nk + 3) & ~3; }
-// Every SAMPLE_STEP-th score of a row is also written to a short contiguous sample row.
-constexpr int SAMPLE_STEP = 16;
-static inline __host__ __device__ int sample_len(int Nk) { return (Nk + SAMPLE_STEP - 1) / SAMPLE_STEP; }
-static inline __host__ __device__ int sample_stride(int Nk) { return (sample_len(Nk) + 3) & ~3; }
 
 int mask_heads_per_pass(int BH, int G, int Nk) {
   const size_t per = (size_t)G * (size_t)score_stride(Nk) * 4;
@@ -624,10 +617,13 @@ static int launch_mask_d(const MaskArgs& a) {
   float* scores = (float*)(ws + 2 * means);
   const int hp = mask_heads_per_pass(BH, G, a.Nk);
   float* samples = (float*)(ws + 2 * means + align256((size_t)hp * G * score_stride(a.Nk) * 4));
-  hipLaunchKernelGGL((k_group_mean<D>), dim3(BH * G), dim3(256), 0, st, (const uint16_t*)a.q, a.Nq, a.group, G,
-                     qhi, qlo);
-  int err = (int)hipGetLastError();
-  if (err) return err;
+  int err = 0;
+  if (a.mode != 2) {   // the column-sum mode scores from the full queries, not their mean
+    hipLaunchKernelGGL((k_group_mean<D>), dim3(BH * G), dim3(256), 0, st, (const uint16_t*)a.q, a.Nq, a.group, G,
+                       qhi, qlo);
+    err = (int)hipGetLastError();
+    if (err) return err;
+  }
   const int gtiles = (G + 127) / 128;                       // quads of 32-group tiles
   const int kchunks = (a.Nk + SC_KT * 32 - 1) / (SC_KT * 32);
   const float log_tau = a.mode == 1 ? (a.thresh > 0.0f ? logf(a.thresh) : -INFINITY) : 0.0f;
@@ -643,12 +639,18 @@ static int launch_mask_d(const MaskArgs& a) {
   }
   for (int bh0 = 0; bh0 < BH; bh0 += hp) {
     const int n = BH - bh0 < hp ? BH - bh0 : hp;
-    hipLaunchKernelGGL((k_scores<D>), dim3(n * gtiles * kchunks), dim3(256), 0, st, (const uint16_t*)a.k, qhi, qlo,
-                       a.Nk, G, a.scale, scores, samples, bh0, gtiles, kchunks);
+    if (a.mode == 2) {
+      ColsumArgs c{a.q, a.k, a.lse, a.Nq, a.Nk, a.D, a.group, a.scale, scores, samples, bh0, n, a.stream};
+      err = launch_colsum_scores(c);
+      if (err) return err;
+    } else {
+      hipLaunchKernelGGL((k_scores<D>), dim3(n * gtiles * kchunks), dim3(256), 0, st, (const uint16_t*)a.k, qhi,
+                         qlo, a.Nk, G, a.scale, scores, samples, bh0, gtiles, kchunks);
+    }
 #define SATTN_SEL(T_)                                                                                     \
   hipLaunchKernelGGL((k_select<T_>), dim3(n * G), dim3(SEL_THREADS), select_lds_bytes(a.Nk, T_), st, scores,    \
                      samples, a.Nk, G, a.topk, log_tau, a.idx, a.counts, a.cap, bh0)
-    if (a.mode == 0) SATTN_SEL(true);
+    if (a.mode != 1) SATTN_SEL(true);
     else SATTN_SEL(false);
 #undef SATTN_SEL
     err = (int)hipGetLastError();

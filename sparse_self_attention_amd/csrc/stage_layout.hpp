@@ -1,0 +1,17 @@
+// Layout of the fp32 per-(group, key) values that the mask kernels stage in the workspace for the
+// per-group selection: one padded row per group, plus a contiguous row of every 16th value.
+#pragma once
+
+#include <stddef.h>
+
+namespace sattn {
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// fp32 score rows are padded to a multiple of 4 floats so 16-byte stores stay aligned
+static inline __host__ __device__ int score_stride(int Nk) { return (Nk + 3) & ~3; }
+// Every SAMPLE_STEP-th score of a row is also written to a short contiguous sample row.
+constexpr int SAMPLE_STEP = 16;
+static inline __host__ __device__ int sample_len(int Nk) { return (Nk + SAMPLE_STEP - 1) / SAMPLE_STEP; }
+static inline __host__ __device__ int sample_stride(int Nk) { return (sample_len(Nk) + 3) & ~3; }
+
+}  // namespace sattn

@@ -36,6 +36,18 @@ def check_out(o_gpu: np.ndarray, o_ref: np.ndarray, what: str):
     return err, rel
 
 
+def check_out_scaled(o_gpu: np.ndarray, o_ref: np.ndarray, what: str):
+    """Like check_out for unnormalised sums (the sparse-delta part with a stale lse): P is rounded to
+    bf16 with a relative error, so the absolute bar scales with the magnitude of the reference."""
+    o_gpu = o_gpu.astype(np.float64)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
+    mag = max(1.0, float(np.abs(o_ref).max()))
+    err = np.abs(o_gpu - o_ref).max()
+    rel = np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-300)
+    assert err <= MAX_ABS * mag and rel <= REL_L2, f"{what}: max|err| {err:.3g} (scale {mag:.3g}) rel-L2 {rel:.3g}"
+    return err, rel
+
+
 def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str):
     l_gpu = l_gpu.astype(np.float64)
     ninf = np.isneginf(l_ref)

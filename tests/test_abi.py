@@ -33,6 +33,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"sattn_mask", "sattn_forward", "attn_forward", "sattn_mask_workspace_bytes", "sattn_cached_mask",
+            "sattn_colsum_mask", "sattn_delta_forward",
             "sattn_strerror", "sattn_last_error", "sattn_voxel_permutation", "sattn_permute_tokens"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sattn.h but not exported"
@@ -113,6 +114,43 @@ CACHED_CASES = [
 def test_cached_mask_validation(lib, kw, code):
     assert cmk(lib, **kw) == code
     assert lib.sattn_last_error()
+
+
+def csm(lib, q=FAKE, k=FAKE, lse=FAKE, B=1, H=1, Nq=128, Nk=128, D=128, group=128, topk=16, scale=0.1,
+        idx=FAKE, counts=FAKE, cap=16, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sattn_colsum_mask(q, k, lse, B, H, Nq, Nk, D, group, topk, scale, idx, counts, cap, ws, ws_bytes, P(0))
+
+
+COLSUM_CASES = [
+    (dict(lse=P(0)), ERR_NULL), (dict(k=P(0)), ERR_NULL), (dict(B=0), ERR_SHAPE), (dict(D=48), ERR_UNSUPPORTED),
+    (dict(group=72), ERR_UNSUPPORTED), (dict(Nk=140000), ERR_UNSUPPORTED), (dict(topk=0), ERR_ARG),
+    (dict(topk=129), ERR_ARG), (dict(cap=15), ERR_ARG), (dict(scale=float("nan")), ERR_ARG),
+    (dict(lse=P(4098)), ERR_ARG), (dict(ws=P(0)), ERR_WORKSPACE), (dict(ws_bytes=8), ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,code", COLSUM_CASES, ids=[str(c[0]) for c in COLSUM_CASES])
+def test_colsum_mask_validation(lib, kw, code):
+    assert csm(lib, **kw) == code
+
+
+def dlt(lib, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, counts=FAKE, cap=64, B=1, H=1, Nq=128, Nk=128, D=128, group=128,
+        scale=0.1, lse=FAKE, out_prev=FAKE, fresh=FAKE, out=FAKE, out_dtype=1):
+    return lib.sattn_delta_forward(q, k, v, idx, counts, cap, B, H, Nq, Nk, D, group, scale, lse, out_prev, fresh,
+                                   out, out_dtype, P(0))
+
+
+DELTA_CASES = [
+    (dict(lse=P(0)), ERR_NULL), (dict(out_prev=P(0)), ERR_NULL), (dict(fresh=P(0)), ERR_NULL), (dict(v=P(0)), ERR_NULL),
+    (dict(Nq=0), ERR_SHAPE), (dict(D=32), ERR_UNSUPPORTED), (dict(group=12), ERR_UNSUPPORTED),
+    (dict(scale=-1.0), ERR_ARG), (dict(cap=0), ERR_ARG), (dict(out_dtype=5), ERR_ARG),
+    (dict(fresh=P(4104)), ERR_ARG), (dict(out_prev=P(4100)), ERR_ARG), (dict(lse=P(4097)), ERR_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", DELTA_CASES, ids=[str(c[0]) for c in DELTA_CASES])
+def test_delta_forward_validation(lib, kw, code):
+    assert dlt(lib, **kw) == code
 
 
 def test_dense_validation(lib):
