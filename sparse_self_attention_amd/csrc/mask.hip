@@ -381,28 +381,34 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       uint32_t u[SEL_UNROLL];
 #pragma unroll
       for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+      // ballots of the batch first, then one LDS atomic reserves the wave's candidate slots for it
+      uint64_t bc[SEL_UNROLL];
+      int nb = 0;
 #pragma unroll
       for (int e = 0; e < SEL_UNROLL; ++e) {
         const int i = i0 + e;
-        if (i < rows) {
-          const uint64_t above = __builtin_amdgcn_ballot_w64(u[e] > key_hi);
-          const bool cand = u[e] != 0u && u[e] >= key_lo && u[e] <= key_hi;
-          const uint64_t bc = __builtin_amdgcn_ballot_w64(cand);
-          int base = 0;
-          if (lane == 0) {
-            const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
-            strict_bits[w0] = (uint32_t)above;
-            strict_bits[w0 + 1] = (uint32_t)(above >> 32);
-            above_w += __popcll(above);
-            if (bc) base = atomicAdd(&ncand, (int)__popcll(bc));
-          }
-          base = __builtin_amdgcn_readfirstlane(base);
-          if (cand) {
-            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bc, 0u));
-            if (pos < SEL_CAND) { cand_key[pos] = u[e]; cand_j[pos] = i * SEL_THREADS + tid; }
-          }
+        const bool in = i < rows;
+        const uint64_t above = __builtin_amdgcn_ballot_w64(in && u[e] > key_hi);
+        bc[e] = __builtin_amdgcn_ballot_w64(in && u[e] != 0u && u[e] >= key_lo && u[e] <= key_hi);
+        nb += (int)__popcll(bc[e]);
+        if (in && lane == 0) {
+          const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
+          strict_bits[w0] = (uint32_t)above;
+          strict_bits[w0 + 1] = (uint32_t)(above >> 32);
+          above_w += __popcll(above);
         }
+      }
+      int base = 0;
+      if (lane == 0 && nb > 0) base = atomicAdd(&ncand, nb);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int e = 0; e < SEL_UNROLL; ++e) {
+        if ((bc[e] >> lane) & 1u) {
+          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc[e] >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bc[e], 0u));
+          if (pos < SEL_CAND) { cand_key[pos] = u[e]; cand_j[pos] = (i0 + e) * SEL_THREADS + tid; }
+        }
+        base += (int)__popcll(bc[e]);
       }
     }
     if (lane == 0) ired[wave] = above_w;
