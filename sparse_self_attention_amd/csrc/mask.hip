@@ -93,12 +93,14 @@ __global__ __launch_bounds__(256) void k_group_mean(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------------------------
 // scores: one wave = 32 groups x (KT x 32) keys
 // ---------------------------------------------------------------------------------------------
-constexpr int SC_KT = 8;   // 32-key tiles per workgroup
+constexpr int SC_KT = 16;   // 32-key tiles per workgroup
 
-// S = q_avg K^T: A = 32 group means (rows = groups), B = K^T (columns = keys).  The 4 waves of a
-// workgroup own 4 different 32-group tiles and walk the same SC_KT x 32 keys, so each K row is
-// fetched once per workgroup.  In the accumulator layout lane l holds key j0 + l%32 for 16 groups:
-// each store instruction writes two contiguous 128-byte runs of score rows.
+// S = q_avg K^T: A = 32 group means (rows = groups, hi and lo halves in VGPRs), B = K^T (columns =
+// keys).  The 4 waves of a workgroup own 4 different 32-group tiles and walk the same SC_KT x 32
+// keys; each 32-key tile is gathered once into LDS with buffer-load-to-LDS (double-buffered, rows
+// XOR-swizzled as in the forward) and read by all four waves.  In the accumulator layout lane l holds
+// key j0 + l%32 for 16 groups: each store instruction writes two contiguous 128-byte runs of score
+// rows.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_scores(const uint16_t* __restrict__ k, const uint16_t* __restrict__ qhi,
                                                  const uint16_t* __restrict__ qlo, int Nk, int G, float scale,
@@ -106,7 +108,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                                  int gtiles, int kchunks) {
   constexpr int KSTEPS = D / 16;
   constexpr int RB = D * 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NC = D / 8;                       // 16-byte chunks per row
+  constexpr int ROWS_PER_LOAD = 1024 / RB;        // rows filled by one 64-lane 16-byte load
+  constexpr int ROWSETS = 32 / ROWS_PER_LOAD;
+  constexpr int NRS = (ROWSETS + 3) / 4;          // row-sets gathered per wave
+  constexpr int TILE = 32 * RB;
+  constexpr int ROWDIV = 16 / NC;
+  __shared__ __attribute__((aligned(1024))) char ktile[2 * TILE];
+  auto swz = [](int row) { return (row / ROWDIV) % NC; };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hi = lane >> 5, ql = lane & 31;
   int t = blockIdx.x;
   const int kc = t % kchunks; t /= kchunks;
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int hh = t / gtiles;               // head inside this pass
   const size_t bh = (size_t)bh0 + hh;
   const int gt = gq * 4 + wave;            // this wave's 32-group tile
-  if (gt * 32 >= G) return;                // no barrier below: a wave may leave early
+  const bool active = gt * 32 < G;         // idle waves still take part in the gathers and barriers
 
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(qhi + bh * G * D, (uint32_t)G * RB);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(qlo + bh * G * D, (uint32_t)G * RB);
@@ -127,26 +138,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     alo[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rl, goff + (2 * ks + hi) * 16));
   }
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * Nk * D, (uint32_t)Nk * RB);
+  uint32_t koff[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = ql * RB + 16 * ((2 * ks + hi) ^ swz(ql));
+  const int row_in = lane / NC, pchunk = lane % NC;
+  uint32_t kch[NRS];
+#pragma unroll
+  for (int j = 0; j < NRS; ++j) kch[j] = 16u * (uint32_t)(pchunk ^ swz((wave + 4 * j) * ROWS_PER_LOAD + row_in));
+  const int jbase = kc * SC_KT * 32;
+  const int ntile = min(SC_KT, (Nk - jbase + 31) / 32);
+  auto issue = [&](int st, int tile) {
+#pragma unroll
+    for (int j = 0; j < NRS; ++j) {
+      const int rs = wave + 4 * j;
+      if (ROWSETS % 4 == 0 || rs < ROWSETS) {
+        const int p = jbase + tile * 32 + rs * ROWS_PER_LOAD + row_in;
+        const uint32_t key = (uint32_t)(p < Nk ? p : Nk - 1);
+        buffer_load_lds_x4(rk, ktile + st * TILE + rs * ROWS_PER_LOAD * RB, key * RB + kch[j]);
+      }
+    }
+  };
   const int stride = score_stride(Nk);
   float* sbase = scores + (size_t)hh * G * stride;
   const int sstride = sample_stride(Nk);
   float* pbase = samples + (size_t)hh * G * sstride;
   const bool sampler = (ql % SAMPLE_STEP) == 0;   // j0 is a multiple of 32, so j % 16 == ql % 16
-  for (int kt = 0; kt < SC_KT; ++kt) {
-    const int j0 = (kc * SC_KT + kt) * 32;
-    if (j0 >= Nk) break;
-    const uint32_t koff = (uint32_t)(j0 + ql) * RB;
-    bf16x8 b[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      b[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rk, koff + (2 * ks + hi) * 16));
+
+  issue(0, 0);
+  for (int tile = 0; tile < ntile; ++tile) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt0();
+    __syncthreads();   // tile landed for every wave; the other stage is free again
+    if (tile + 1 < ntile) issue((tile + 1) & 1, tile + 1);
+    if (!active) continue;
+    const char* kt = ktile + (tile & 1) * TILE;
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], b[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], b[ks], acc, 0, 0, 0);
+      const bf16x8 b = *(const bf16x8*)(kt + koff[ks]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], b, acc, 0, 0, 0);
     }
-    const int j = j0 + ql;
+    const int j = jbase + tile * 32 + ql;
     if (j < Nk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
