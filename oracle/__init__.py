@@ -21,10 +21,16 @@ Readings of passages that the pages leave open:
     full-attention softmax probability of at least tau; tau <= 0 keeps every
     key and a group may keep none;
   * the Chipmunk sparse delta uses the full-softmax form the review asks for:
-    probabilities with a stale lse, no renormalisation over the selected keys.
+    probabilities with a stale lse, no renormalisation over the selected keys;
+  * the FP8 value path takes bf16 block means, power-of-two channel scales, a
+    reference point on the 1/8 grid of log2 units moved only when a block's max
+    exceeds it by more than 3/4, and ExpCast bytes with the probability scaled by
+    2^8 (bias 120 instead of 56); oracle/fp8.py states each.
 """
 from .attention import dense_attention_ref, sparse_attention_ref, sparse_attention_probs_ref  # noqa: F401
 from .mask import (group_mean_ref, group_scores_ref, topk_select_ref, thresh_select_ref,  # noqa: F401
                    mask_ref)
 from .cached import (row_lse_ref, slice_max_logprob_ref, cached_mask_ref, colsum_scores_ref,  # noqa: F401
                      colsum_mask_ref, delta_fresh_ref, delta_forward_ref)
+from .fp8 import (e4m3_decode_table, e4m3_encode, bf16_round, channel_scale_exponent,  # noqa: F401
+                  vsmooth_quantize_ref, expcast_byte, dequantize_ref, fp8_attention_ref)

@@ -454,3 +454,223 @@ def check_delta(delta_fresh, delta_forward):
     c0[0, 0, 0] = 0
     f0 = delta_fresh(q, k, v, idx, c0, M, scale, lse)
     assert np.all(f0[0, 0, :M] == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# FP8 value path: E4M3 codes, V-Smooth quantisation, ExpCast, the FP8 attention
+# ----------------------------------------------------------------------------
+
+def check_e4m3(decode_table, encode):
+    """Code values from the E4M3 definition (OCP 8-bit floating point spec): exponent bias 7,
+    subnormals m/8 * 2^-6, S.1111.111 NaN, largest 448; nearest-even rounding and saturation."""
+    t = decode_table()
+    spec = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+            0x3C: 1.5, 0x40: 2.0, 0x4B: 2.0 ** 2 * 1.375, 0x77: 2.0 ** 7 * 1.875, 0x7E: 448.0, 0xB8: -1.0,
+            0xFE: -448.0}
+    for c, v in spec.items():
+        assert t[c] == v, (hex(c), t[c], v)
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+    # every finite non-negative code round-trips
+    codes = np.array([c for c in range(127)], dtype=np.uint8)
+    assert np.array_equal(encode(t[codes]), codes)
+    # brute-force nearest code (ties to even) on random magnitudes, and saturation
+    rng = np.random.default_rng(41)
+    x = np.concatenate([rng.uniform(-500, 500, 300), rng.uniform(-1, 1, 300), rng.uniform(-0.02, 0.02, 300)])
+    got = encode(x)
+    finite = np.array([c for c in range(256) if not math.isnan(t[c])])
+    for xi, gi in zip(x, got):
+        xs = min(max(xi, -448.0), 448.0)
+        d = np.abs(t[finite] - xs)
+        best = finite[d == d.min()]
+        if best.size > 1:                               # a tie: the even code wins (same sign)
+            best = best[(best % 2 == 0)]
+        assert t[gi] == t[best[0]], (xi, hex(gi), [hex(b) for b in best])
+    mid = (t[0x38] + t[0x39]) / 2                        # 1.0625 lies between codes 56 and 57
+    assert encode([mid])[0] == 0x38 and encode([(t[0x39] + t[0x3A]) / 2])[0] == 0x3A
+
+
+def check_expcast(expcast, decode_table):
+    """The V-Smart/ExpCast summary's figures: over the normal E4M3 range the byte from 8 x + 56 (here
+    with the 2^8 probability scale, 8 x + 120) is never more than one code from the exactly rounded
+    code of 2^(x + 8) (how often it is exact depends on the distribution of x: about half the time
+    for uniform x, 79.6 % on the summary's attention scores, which are not available here); the
+    probabilities it gives have a per-row total variation from the exact softmax below 3.64 %."""
+    from scipy.special import softmax
+    t = decode_table()
+    rng = np.random.default_rng(43)
+    x = rng.uniform(-14.0, 0.0, 20000)
+    b = expcast(x).astype(np.int64)
+    exact = np.array([int(np.argmin(np.abs(t[:127] - 2.0 ** (xi + 8)))) for xi in x])
+    diff = np.abs(b - exact)
+    assert diff.max() <= 1
+    assert 0.4 <= float((diff == 0).mean()) <= 0.7
+    assert expcast([-15.2])[0] == 0 and expcast([0.0])[0] == 120 and expcast([0.75])[0] == 126
+    for _ in range(50):
+        s = rng.standard_normal(400) * 3.0
+        x2 = (s - s.max()) / math.log(2.0)
+        p = t[expcast(x2)]
+        tv = 0.5 * np.abs(p / p.sum() - softmax(s)).sum()
+        assert tv < 0.0364, tv
+
+
+def _nearest_bf16(x):
+    """Nearest bf16 value of a Fraction by brute force on its binade grid, ties to the even multiple."""
+    from fractions import Fraction
+    if x == 0:
+        return 0.0
+    e = math.floor(math.log2(abs(float(x))))
+    while Fraction(2) ** e > abs(x):
+        e -= 1
+    while Fraction(2) ** (e + 1) <= abs(x):
+        e += 1
+    ulp = Fraction(2) ** (e - 7)
+    lo = math.floor(x / ulp)
+    d_lo, d_hi = x - lo * ulp, (lo + 1) * ulp - x
+    n = lo if (d_lo < d_hi or (d_lo == d_hi and lo % 2 == 0)) else lo + 1
+    return float(n * ulp)
+
+
+def _bf16_values(rng, shape, sd=1.0):
+    from synth import inputs
+    return inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(rng.standard_normal(shape) * sd)).astype(np.float64)
+
+
+def check_vsmooth(vsmooth, decode_table):
+    """V-Smooth quantisation against brute force: exact block means (rational arithmetic) rounded to
+    the nearest bf16, the ragged last block averaged over its own tokens only, power-of-two channel
+    scales that put the largest residual in (224, 448], and every code the nearest E4M3 value of the
+    fp32 residual over the scale; a constant channel has scale 1 and all-zero codes."""
+    from fractions import Fraction
+    t = decode_table()
+    rng = np.random.default_rng(53)
+    B, H, N, D = 1, 2, 300, 6                       # blocks of 128, 128 and a ragged 44
+    v = _bf16_values(rng, (B, H, N, D))
+    v[0, 0] += np.repeat(np.array([3.0, -2.5, 0.75]), [128, 128, 44])[:, None]   # block offsets
+    v[0, 1, :, 2] = 1.5                              # a constant channel
+    v[0, 1, 128:256, 3] = 1.0                        # block mean 1 + 2^-8: a bf16 tie, to even (1.0)
+    v[0, 1, 128, 3] = 1.5
+    codes, scale, mean = vsmooth(v)
+    assert codes.shape == (B, H, N, D) and codes.dtype == np.uint8
+    assert scale.shape == (B, H, D) and mean.shape == (B, H, 3, D)
+    finite = np.array([c for c in range(256) if not math.isnan(t[c])])
+    for h in range(H):
+        for blk, (a, z) in enumerate([(0, 128), (128, 256), (256, 300)]):
+            for d in range(D):
+                exact = sum(Fraction(float(x)) for x in v[0, h, a:z, d]) / (z - a)
+                assert mean[0, h, blk, d] == _nearest_bf16(exact), (h, blk, d)
+        for d in range(D):
+            r = np.array([np.float32(v[0, h, n, d]) - np.float32(mean[0, h, n // 128, d]) for n in range(N)],
+                         dtype=np.float32).astype(np.float64)
+            s = scale[0, h, d]
+            e = math.log2(s)
+            assert e == round(e), s
+            amax = np.abs(r).max()
+            if amax == 0:
+                assert s == 1.0 and not codes[0, h, :, d].any()
+                continue
+            assert 224.0 < amax / s <= 448.0, (h, d, amax, s)
+            for n in range(0, N, 7):
+                x = r[n] / s
+                dist = np.abs(t[finite] - x)
+                best = finite[dist == dist.min()]
+                if best.size > 1:
+                    best = best[best % 2 == 0]
+                assert t[codes[0, h, n, d]] == t[best[0]], (h, n, d, x)
+    assert (scale[0, 1, 2] == 1.0) and not codes[0, 1, :, 2].any() and mean[0, 1, 0, 2] == 1.5
+    assert mean[0, 1, 1, 3] == 1.0
+
+
+def _fp8_brute_row(s2, vrows, t):
+    """One row by explicit loops: the reference point m8 / 8 on the 1/8 grid, set by the first block of
+    64 and moved to ceil8(block max) only past m + 3/4, weights E4M3(round(8 s2 - m8 + 120))."""
+    m8, w, moves = None, {}, 0
+    for j0 in range(0, len(s2), 64):
+        bm = max(s2[j0:j0 + 64])
+        if m8 is None:
+            m8 = math.ceil(8 * bm)
+        elif bm > m8 / 8 + 0.75:
+            new = math.ceil(8 * bm)
+            for jj in w:
+                w[jj] *= 2.0 ** ((m8 - new) / 8)
+            m8, moves = new, moves + 1
+        for jj in range(j0, min(j0 + 64, len(s2))):
+            w[jj] = t[min(max(round(8 * s2[jj] - m8 + 120), 0), 126)]      # round(): half to even
+    _fp8_brute_row.moves = moves
+    l = math.fsum(w.values())
+    out = np.array([math.fsum(w[jj] * vrows[jj, d] for jj in w) / l for d in range(vrows.shape[1])])
+    return out, math.log(l) + (m8 / 8 - 8) * math.log(2.0)
+
+
+def check_fp8_attention(vsmooth, fp8_attn, decode_table, dequant):
+    """The FP8 attention path: per-element loops with the row's reference point on the 1/8 grid (moved
+    only past 3/4), bytes round-half-even(8 (x - m) + 120) and the decoded value rows; equal scores give
+    the plain mean of the listed value rows and lse = ln c; one key gives its value row; and the
+    output and lse stay within the ExpCast error of the exact restricted softmax over the same
+    dequantised values (the summary's 3.64 % total-variation bound), with large per-block means."""
+    t = decode_table()
+    rng = np.random.default_rng(47)
+    B, H, Nq, Nk, D, M = 1, 2, 20, 300, 16, 8
+    q, k, _ = _rand_qkv(rng, B, H, Nq, Nk, D, scale_q=2.5)
+    v = _bf16_values(rng, (B, H, Nk, D))
+    v[0, :, :128] += 4.0
+    v[0, :, 128:256] -= 3.0
+    scale = 1.0 / math.sqrt(D)
+    codes, vs, vm = vsmooth(v)
+    vhat = np.zeros((B, H, Nk, D))
+    for h in range(H):
+        for j in range(Nk):
+            for d in range(D):
+                vhat[0, h, j, d] = t[codes[0, h, j, d]] * vs[0, h, d] + vm[0, h, j // 128, d]
+    assert np.array_equal(dequant(codes, vs, vm), vhat)
+    G = -(-Nq // M)
+    idx, cnt = _random_lists(rng, B, H, G, Nk, 230)
+    cnt[0, 0, 0], cnt[0, 1, 1] = 230, 65
+    out, lse = fp8_attn(q, k, codes, vs, vm, idx, cnt, M, scale)
+    ln2 = math.log(2.0)
+    for h in range(H):
+        for i in range(Nq):
+            g = i // M
+            J = [int(j) for j in idx[0, h, g, :cnt[0, h, g]]]
+            s2 = [math.fsum(q[0, h, i, d] * k[0, h, j, d] for d in range(D)) * scale / ln2 for j in J]
+            want, want_lse = _fp8_brute_row(s2, vhat[0, h, J], t)
+            assert np.all(np.abs(out[0, h, i] - want) <= 1e-10 * (1 + np.abs(want))), (h, i)
+            assert abs(lse[0, h, i] - want_lse) <= 1e-10
+            # the exact restricted softmax over the same dequantised rows
+            ex = np.exp(np.array(s2) * ln2 - max(s2) * ln2)
+            pe = ex / ex.sum()
+            exact = pe @ vhat[0, h, J]
+            assert np.abs(out[0, h, i] - exact).max() <= 2 * 0.0364 * np.abs(vhat[0, h, J]).max()
+            exact_lse = max(s2) * ln2 + math.log(ex.sum())
+            assert abs(lse[0, h, i] - exact_lse) <= 0.15 * ln2
+    # scores rising along the list: by 1/5 per block of 64 (the reference point stays, bytes climb past
+    # 120) and by 5/4 per block (it moves every block and the earlier weights are carried over)
+    for slope, moves in ((0.2 / 64, 0), (1.25 / 64, 3)):
+        kr = np.zeros((1, 1, 256, 4))
+        kr[0, 0, :, 0] = np.arange(256) * slope * ln2 - 3.0
+        kr[0, 0, :, 1] = rng.standard_normal(256) * 0.05
+        qr = np.zeros((1, 1, 8, 4))
+        qr[0, 0, :, 0] = 1.0
+        qr[0, 0, :, 1] = np.linspace(-1, 1, 8)
+        cr, sr, mr = vsmooth(_bf16_values(rng, (1, 1, 256, 4)))
+        vr = dequant(cr, sr, mr)
+        idxr = np.arange(256, dtype=np.int32).reshape(1, 1, 1, 256)
+        outr, lser = fp8_attn(qr, kr, cr, sr, mr, idxr, np.full((1, 1, 1), 256, np.int32), 8, 1.0)
+        for i in range(8):
+            s2 = [float(qr[0, 0, i] @ kr[0, 0, j]) / ln2 for j in range(256)]
+            want, want_lse = _fp8_brute_row(s2, vr[0, 0], t)
+            assert _fp8_brute_row.moves == moves, (slope, _fp8_brute_row.moves)
+            assert np.all(np.abs(outr[0, 0, i] - want) <= 1e-10 * (1 + np.abs(want))) and abs(lser[0, 0, i] - want_lse) <= 1e-10
+    # equal scores (q = 0): every byte is 120, so the output is the plain mean of the listed rows
+    out0, lse0 = fp8_attn(np.zeros_like(q), k, codes, vs, vm, idx, cnt, M, scale)
+    for h in range(H):
+        for g in range(G):
+            J = idx[0, h, g, :cnt[0, h, g]]
+            assert np.allclose(out0[0, h, g * M:(g + 1) * M], vhat[0, h, J].mean(axis=0), atol=1e-12)
+            assert np.allclose(lse0[0, h, g * M:(g + 1) * M], math.log(len(J)), atol=1e-12)
+    # one listed key: its dequantised row; empty list: zeros and -inf
+    idx1 = np.full((B, H, G, 1), 200, dtype=np.int32)
+    cnt1 = np.ones((B, H, G), dtype=np.int32)
+    cnt1[0, 1, 0] = 0
+    out1, lse1 = fp8_attn(q, k, codes, vs, vm, idx1, cnt1, M, scale)
+    assert np.allclose(out1[0, 0], vhat[0, 0, 200], atol=1e-12)
+    assert not out1[0, 1, :M].any() and np.all(np.isneginf(lse1[0, 1, :M]))

@@ -103,6 +103,36 @@ DELTA_MUTANTS = [
 ]
 
 
+FP8_MUTANTS = [
+    ("ExpCast bias without the 2^8 scale", "EXPCAST_BIAS = 56.0 + 64.0", "EXPCAST_BIAS = 56.0 + 56.0"),
+    ("ExpCast truncates", "b = np.rint(y)", "b = np.floor(y)"),
+    ("reference point off the 1/8 grid", "m8 = np.ceil(8.0 * bm)\n", "m8 = 8.0 * bm\n"),
+    ("reference point kept past saturation", "RESCALE_SLACK = 0.75", "RESCALE_SLACK = 2.0"),
+    ("earlier blocks not rescaled", "o *= alpha[:, None]", "o *= 1.0"),
+    ("block mean not restored", "return _DEC[codes] * scale[:, :, None, :] + mean[:, :, np.arange(N) // VS_BLOCK, :]",
+     "return _DEC[codes] * scale[:, :, None, :]"),
+    ("one mean per head", "VS_BLOCK = 128", "VS_BLOCK = 1 << 20"),
+    ("mean not rounded to bf16", "mean[b, h, blk, d] = bf16_round(math.fsum(rows[:, d]) / rows.shape[0])",
+     "mean[b, h, blk, d] = math.fsum(rows[:, d]) / rows.shape[0]"),
+    ("channel scale not a power of two", "scale = np.ldexp(1.0, e)", "scale = np.where(amax > 0, amax / 448.0, 1.0)"),
+    ("lse without the 2^-8", "(np.log2(l) + m8 / 8.0 - 8.0) / log2e", "(np.log2(l) + m8 / 8.0) / log2e"),
+    ("E4M3 exponent bias 8", "else (1.0 + m / 8.0) * 2.0 ** (e - 7)", "else (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    ("ties away from even", "((dhi == dlo) & (hi % 2 == 0))", "(dhi == dlo)"),
+    ("bf16 ties away from even", "if frac > 0.5 or (frac == 0.5 and r % 2 == 1):", "if frac >= 0.5:"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", FP8_MUTANTS, ids=[m[0] for m in FP8_MUTANTS])
+def test_fp8_mutant_is_caught(name, old, new):
+    m = _mutant("oracle.fp8", old, new)
+    checks = [lambda: pins.check_e4m3(m.e4m3_decode_table, m.e4m3_encode),
+              lambda: pins.check_expcast(m.expcast_byte, m.e4m3_decode_table),
+              lambda: pins.check_vsmooth(m.vsmooth_quantize_ref, m.e4m3_decode_table),
+              lambda: pins.check_fp8_attention(m.vsmooth_quantize_ref, m.fp8_attention_ref, m.e4m3_decode_table,
+                                               m.dequantize_ref)]
+    assert _caught(checks), f"no pin catches the planted mistake: {name}"
+
+
 @pytest.mark.parametrize("name,old,new", DELTA_MUTANTS, ids=[m[0] for m in DELTA_MUTANTS])
 def test_delta_mutant_is_caught(name, old, new):
     m = _mutant("oracle.cached", old, new)
