@@ -299,6 +299,22 @@ def main():
         rec["chipmunk_delta"] = {"colsum_mask_ms": round(cs_ms, 3), "delta_fwd_ms": round(d_ms, 3),
                                  "delta_kept_tflops": round(kflops / (d_ms * 1e-3) / 1e12, 2)}
         del out_prev, fresh, dout
+        # FP8 value path on the same step and lists: V-Smooth quantisation of V, then the forward with
+        # ExpCast bytes and the E4M3 P.V product; its distance from the bf16 path's output
+        vws = torch.empty(sattn.vsmooth_workspace_bytes(1, w.heads, w.n_k, w.dim), dtype=torch.uint8, device=dev)
+        codes, vscale, vmean = sattn.vsmooth_quantize(v, workspace=vws)
+        q8_ms = timed(lambda: sattn.vsmooth_quantize(v, codes=codes, vscale=vscale, vmean=vmean, workspace=vws))
+        o8 = torch.empty_like(q0)
+        f8_ms = timed(lambda: sattn.fp8_forward(q0, k0, codes, vscale, vmean, idx, counts, w.group, out=o8, lse=lse))
+        sattn.forward(q0, k0, v, idx, counts, w.group, out=out, lse=lse)
+        bf_ms = timed(lambda: sattn.forward(q0, k0, v, idx, counts, w.group, out=out, lse=lse))
+        rel8 = ((o8.float() - out.float()).norm() / out.float().norm()).item()
+        rec["fp8_expcast"] = {"vsmooth_ms": round(q8_ms, 3), "fwd_ms": round(f8_ms, 3),
+                              "bf16_fwd_ms_same_lists": round(bf_ms, 3),
+                              "kept_tflops": round(kflops / (f8_ms * 1e-3) / 1e12, 2),
+                              "speedup_vs_bf16_fwd": round(bf_ms / f8_ms, 3),
+                              "rel_l2_vs_bf16_out": round(rel8, 5)}
+        del vws, codes, vscale, vmean, o8
     if not args.no_cpu_baseline and not args.kernel_only:
         # oracle on the step-0 inputs with the step-0 lists
         sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)

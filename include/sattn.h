@@ -186,6 +186,50 @@ int attn_forward(const void* q, const void* k, const void* v,
                  void* out, int out_dtype, float* lse, void* stream);
 
 /*
+ * FP8 value path (V-Smart/ExpCast summary, its V-Smooth and ExpCast-FP8 paragraphs).
+ *
+ * sattn_vsmooth_quantize - V-Smooth quantisation of V for sattn_fp8_forward.  Per block of 128
+ * tokens (the last block may be shorter) and channel, the exact mean of the bf16 tokens is
+ * rounded to bf16 (nearest even); the fp32 residual v - mean is divided by the channel scale
+ * s = 2^e, the smallest power of two with 448 * s >= max |residual| over the head (1 when the
+ * residual is 0), and rounded to E4M3 (OCP "fn" encoding, nearest even).
+ *   v       bf16 [B,H,Nk,D], 16-byte aligned.
+ *   codes   out: uint8 [B,H,Nk,D] E4M3 codes, 16-byte aligned.
+ *   vscale  out: fp32 [B,H,D] channel scales (powers of two), 16-byte aligned.
+ *   vmean   out: bf16 [B,H,D,S] with S = sattn_vsmooth_mean_stride(Nk), 16-byte aligned:
+ *           entry [b,h,d,blk] = mean of block blk / vscale[b,h,d] (exact); entries past the last
+ *           block are 0.  Channel-major so that the forward reads a window of 32 blocks per channel.
+ *   workspace device scratch of sattn_vsmooth_workspace_bytes(B,H,Nk,D) bytes, 256-byte aligned.
+ * The block mean equals the rounded exact mean when the tokens of a block span fewer than 2^45
+ * in magnitude (the fp64 sum is then exact).  Errors: NULL pointers, D not 64/128, bad sizes or
+ * alignment, workspace too small.
+ */
+size_t sattn_vsmooth_workspace_bytes(int B, int H, int Nk, int D);
+int sattn_vsmooth_mean_stride(int Nk);   /* 4 * ceil(ceil(Nk / 128) / 4); 0 if Nk < 1 */
+int sattn_vsmooth_quantize(const void* v, int B, int H, int Nk, int D, uint8_t* codes, float* vscale,
+                           void* vmean, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sattn_fp8_forward - sparse forward over per-group key lists with ExpCast probability bytes and
+ * an E4M3 P.V product, on V quantised by sattn_vsmooth_quantize.
+ *
+ * For query row i of group g with listed keys J (list order, blocks of 64): s = scale q_i.k_j in
+ * log2 units; the row's reference point m (a multiple of 1/8) is ceil8 of the first block's max
+ * and moves to ceil8(block max) only when a block's max exceeds m + 3/4 (earlier sums are then
+ * scaled by 2^(m_old - m_new)); the probability is the E4M3 byte round-half-even(8 (s - m) + 120)
+ * clamped to [0, 126] (the summary's 8 log2 v + 56 with the probability scaled by 2^8);
+ *     out[i] = sum_j p_j (vscale * E4M3(codes[j]) + mean_block(j)) / sum_j p_j,
+ *     lse[i] = ln(sum_j p_j) + (m - 8) ln 2.
+ *   q, k, idx, counts, cap, group, scale, out, out_dtype, lse: as sattn_forward (same list
+ *   preconditions); codes, vscale, vmean: the outputs of sattn_vsmooth_quantize for V.
+ * Errors: as sattn_forward; codes, vscale and vmean must be 16-byte aligned.
+ */
+int sattn_fp8_forward(const void* q, const void* k, const uint8_t* codes, const float* vscale,
+                      const void* vmean, const int32_t* idx, const int32_t* counts, int cap,
+                      int B, int H, int Nq, int Nk, int D, int group, float scale,
+                      void* out, int out_dtype, float* lse, void* stream);
+
+/*
  * sattn_voxel_permutation - host-side token order that makes every run of vt*vy*vx tokens one
  * spatio-temporal voxel of a (T, Hg, Wg) raster grid.
  * Chipmunk review, "What carries the argument" and Fig. 2 caption (voxel reordering so that

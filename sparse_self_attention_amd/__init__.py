@@ -11,6 +11,8 @@ missing or cannot be loaded, every call raises.
     idx, counts = cached_mask(q, k, lse, group=128)        # slices with a probability >= 0.5/N
     idx, counts = colsum_mask(q, k, lse, group=192, topk=k)  # Chipmunk column-sum selection
     out = delta_forward(q, k, v, idx, counts, 192, lse=lse, out_prev=out, fresh=fresh)  # sparse delta
+    codes, vscale, vmean = vsmooth_quantize(v)             # V-Smooth E4M3 codes, scales, block means
+    out, lse    = fp8_forward(q, k, codes, vscale, vmean, idx, counts, group=128)   # ExpCast + FP8 P.V
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["mask", "forward", "attn", "cached_mask", "colsum_mask", "delta_forward", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
+__all__ = ["mask", "forward", "attn", "cached_mask", "colsum_mask", "delta_forward", "vsmooth_quantize",
+           "fp8_forward", "vsmooth_workspace_bytes", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
            "library_path", "SattnError", "TOPK", "THRESH"]
 
 TOPK, THRESH = 0, 1
@@ -66,6 +69,14 @@ def _load():
     lib.sattn_colsum_mask.restype = I
     lib.sattn_delta_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, P, I, P]
     lib.sattn_delta_forward.restype = I
+    lib.sattn_vsmooth_workspace_bytes.argtypes = [I, I, I, I]
+    lib.sattn_vsmooth_workspace_bytes.restype = Z
+    lib.sattn_vsmooth_mean_stride.argtypes = [I]
+    lib.sattn_vsmooth_mean_stride.restype = I
+    lib.sattn_vsmooth_quantize.argtypes = [P, I, I, I, I, P, P, P, P, Z, P]
+    lib.sattn_vsmooth_quantize.restype = I
+    lib.sattn_fp8_forward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, P]
+    lib.sattn_fp8_forward.restype = I
     lib.sattn_voxel_permutation.argtypes = [I, I, I, I, I, I, P]
     lib.sattn_voxel_permutation.restype = I
     lib.sattn_permute_tokens.argtypes = [P, P, P, I, I, I, I, I, P]
@@ -261,6 +272,69 @@ def delta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
                                  F32 if out.dtype == torch.float32 else BF16, _stream_ptr(q))
     _check("sattn_delta_forward", st)
     return out
+
+
+def vsmooth_workspace_bytes(B: int, H: int, Nk: int, D: int) -> int:
+    return int(_load().sattn_vsmooth_workspace_bytes(B, H, Nk, D))
+
+
+def vsmooth_quantize(v: torch.Tensor, *, codes: Optional[torch.Tensor] = None, vscale: Optional[torch.Tensor] = None,
+                     vmean: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """V-Smooth quantisation (sattn_vsmooth_quantize): returns (codes uint8 [B,H,Nk,D], vscale fp32 [B,H,D],
+    vmean bf16 [B,H,D,S] = block mean / vscale, channel-major, S = sattn_vsmooth_mean_stride(Nk))."""
+    lib = _load()
+    if not v.is_cuda or v.dtype != torch.bfloat16 or v.dim() != 4 or not v.is_contiguous():
+        raise ValueError("v must be a contiguous bf16 [B, H, N, D] device tensor")
+    B, H, Nk, D = v.shape
+    S = lib.sattn_vsmooth_mean_stride(Nk)
+    if codes is None:
+        codes = torch.empty((B, H, Nk, D), dtype=torch.uint8, device=v.device)
+    if vscale is None:
+        vscale = torch.empty((B, H, D), dtype=torch.float32, device=v.device)
+    if vmean is None:
+        vmean = torch.empty((B, H, D, S), dtype=torch.bfloat16, device=v.device)
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, Nk, D) or vscale.dtype != torch.float32
+            or tuple(vscale.shape) != (B, H, D) or vmean.dtype != torch.bfloat16 or tuple(vmean.shape) != (B, H, D, S)
+            or not (codes.is_contiguous() and vscale.is_contiguous() and vmean.is_contiguous())):
+        raise ValueError("codes, vscale, vmean: contiguous uint8 [B,H,Nk,D], fp32 [B,H,D], bf16 [B,H,D,S]")
+    need = lib.sattn_vsmooth_workspace_bytes(B, H, Nk, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+    st = lib.sattn_vsmooth_quantize(_ptr(v), B, H, Nk, D, _ptr(codes), _ptr(vscale), _ptr(vmean), _ptr(workspace),
+                                    workspace.numel(), _stream_ptr(v))
+    _check("sattn_vsmooth_quantize", st)
+    return codes, vscale, vmean
+
+
+def fp8_forward(q: torch.Tensor, k: torch.Tensor, codes: torch.Tensor, vscale: torch.Tensor, vmean: torch.Tensor,
+                idx: torch.Tensor, counts: torch.Tensor, group: int, *, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.float32, want_lse: bool = True):
+    """Sparse forward with ExpCast bytes and the E4M3 P.V product (sattn_fp8_forward).  Returns (out, lse)."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k)
+    G = -(-Nq // group)
+    S = lib.sattn_vsmooth_mean_stride(Nk)
+    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
+        raise ValueError("idx and counts must be contiguous int32")
+    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
+        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, Nk, D) or vscale.dtype != torch.float32
+            or tuple(vscale.shape) != (B, H, D) or vmean.dtype != torch.bfloat16 or tuple(vmean.shape) != (B, H, D, S)
+            or not (codes.is_contiguous() and vscale.is_contiguous() and vmean.is_contiguous())):
+        raise ValueError("codes, vscale, vmean must be what vsmooth_quantize returns for a V shaped like k")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or fp32 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = lib.sattn_fp8_forward(_ptr(q), _ptr(k), _ptr(codes), _ptr(vscale), _ptr(vmean), _ptr(idx), _ptr(counts),
+                               idx.shape[-1], B, H, Nq, Nk, D, group, scale, _ptr(out),
+                               F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
+    _check("sattn_fp8_forward", st)
+    return out, lse
 
 
 def voxel_permutation(grid, voxel) -> torch.Tensor:

@@ -226,6 +226,58 @@ int sattn_delta_forward(const void* q, const void* k, const void* v, const int32
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
 
+size_t sattn_vsmooth_workspace_bytes(int B, int H, int Nk, int D) {
+  if (B < 1 || H < 1 || Nk < 1 || (D != 64 && D != 128) || (int64_t)B * H >= I32_MAX) return 0;
+  return sattn::vsmooth_workspace_bytes(B * H, Nk, D);
+}
+
+int sattn_vsmooth_mean_stride(int Nk) { return Nk < 1 ? 0 : sattn::vsmooth_mean_stride(Nk); }
+
+int sattn_vsmooth_quantize(const void* v, int B, int H, int Nk, int D, uint8_t* codes, float* vscale, void* vmean,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  static const char* fn = "sattn_vsmooth_quantize";
+  if (!v || !codes || !vscale || !vmean) return fail(SATTN_ERR_NULL, "%s: v, codes, vscale and vmean must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, 1, Nk, D)) return r;
+  if ((int64_t)B * H * sattn::vsmooth_blocks(Nk) >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many blocks", fn);
+  if (!aligned(v, 16) || !aligned(codes, 16) || !aligned(vscale, 16) || !aligned(vmean, 16))
+    return fail(SATTN_ERR_ARG, "%s: v, codes, vscale and vmean must be 16-byte aligned", fn);
+  const size_t need = sattn_vsmooth_workspace_bytes(B, H, Nk, D);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(SATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-byte aligned), got %zu", fn, need, ws_bytes);
+  sattn::VsmoothArgs a{v, B, H, Nk, D, codes, vscale, vmean, workspace, stream};
+  const int err = sattn::launch_vsmooth(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
+int sattn_fp8_forward(const void* q, const void* k, const uint8_t* codes, const float* vscale, const void* vmean,
+                      const int32_t* idx, const int32_t* counts, int cap, int B, int H, int Nq, int Nk, int D,
+                      int group, float scale, void* out, int out_dtype, float* lse, void* stream) {
+  static const char* fn = "sattn_fp8_forward";
+  if (!q || !k || !codes || !vscale || !vmean || !idx || !counts || !out)
+    return fail(SATTN_ERR_NULL, "%s: q, k, codes, vscale, vmean, idx, counts and out must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
+  if (int r = check_group(fn, group)) return r;
+  if (int r = check_scale(fn, scale)) return r;
+  if (cap < 1) return fail(SATTN_ERR_ARG, "%s: cap = %d must be >= 1", fn, cap);
+  if (out_dtype != SATTN_BF16 && out_dtype != SATTN_F32) return fail(SATTN_ERR_ARG, "%s: bad out_dtype", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(codes, 16) || !aligned(vscale, 16) || !aligned(vmean, 16) ||
+      !aligned(out, 16) || !aligned(idx, 4) || !aligned(counts, 4) || !aligned(lse, 4))
+    return fail(SATTN_ERR_ARG, "%s: q, k, codes, vscale, vmean, out must be 16-byte aligned; idx, counts, lse 4-byte",
+                fn);
+  const int64_t G = (Nq + group - 1) / group;
+  if ((int64_t)B * H * G >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many groups", fn);
+  if (validate_mode()) {
+    int flag = 0;
+    const int err = sattn::validate_index_lists(idx, counts, cap, (int)(B * H * G), Nk, stream, &flag);
+    if (err) return hip_fail(err, fn);
+    if (flag) return fail(SATTN_ERR_INDEX, "%s: index lists invalid (code %d)", fn, flag);
+  }
+  sattn::Fp8FwdArgs a{q, k, codes, vscale, vmean, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out,
+                      out_dtype == SATTN_F32, lse, stream};
+  const int err = sattn::launch_fp8_fwd(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
 int attn_forward(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, int D, float scale,
                  void* out, int out_dtype, float* lse, void* stream) {
   static const char* fn = "attn_forward";

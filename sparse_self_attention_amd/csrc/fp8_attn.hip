@@ -1,0 +1,539 @@
+// FP8 value path for gfx950: V-Smooth quantisation of V and the sparse forward with ExpCast
+// probabilities and an FP8 P.V product.
+//
+// What is computed (V-Smart/ExpCast summary, its V-Smooth and ExpCast-FP8 paragraphs):
+//  * V-Smooth: per block of 128 tokens and channel the mean is subtracted (kept as bf16, 16 bits
+//    per 128 elements) and the residual is quantised to E4M3 with one scale per channel; the
+//    mean returns through the softmax row sums.  The channel scale is the power of two 2^e with
+//    the smallest e such that 448 * 2^e covers the largest residual, so residual / scale and
+//    mean / scale are exact.
+//  * ExpCast: the probability byte is one multiply-add of the raw score plus an integer,
+//    round-half-even(8 (x - m) + 120) clamped to [0, 126], where x is the score in log2 units and
+//    m the row's reference point.  m lies on the 1/8 grid: set by the first block of 64 listed keys
+//    as ceil8(block max), moved to ceil8(block max) only when a block's max exceeds m + 3/4 (the
+//    largest byte then stays <= 126), the earlier sums scaled by 2^(m_old - m_new).  The bias
+//    120 = 56 + 64 carries the probability scaled by 2^8.
+//
+// Mapping onto CDNA4
+// ------------------
+//  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32).  Tiles of 64
+//    listed keys: K rows (bf16) and V rows (E4M3, D bytes) are gathered from HBM into LDS with
+//    16-byte buffer-load-to-LDS instructions, double-buffered.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 as in the bf16 path (two 32-key halves); each lane
+//    owns one query row and 32 of the 64 keys, so the block max is in-lane plus one lane-pair
+//    exchange, and the 32 probability bytes of a lane are exactly the B operand of
+//    v_mfma_f32_32x32x64_f8f6f4 for its row: no register shuffle between the two products.
+//    Byte b = 16 s + r of lane (row, h) holds key 32 s + 8 (r / 4) + 4 h + r % 4.
+//  * The byte: y = fma(score, 8 scale log2e, 1.5 * 2^23 + 120 - 8m) puts round-half-even(8 (x - m)
+//    + 120) in the low mantissa bits, and an integer subtract and clamp give the byte.  One fp32
+//    operation per probability instead of an exp, a conversion and a sum.
+//  * O^T += V8^T P^T: A = the V codes read from LDS with ds_read_b64_tr_b8 (the gfx950 transposing
+//    byte read), four 8-byte reads per 64-key tile and 32 output dims.  Rows are XOR-swizzled in
+//    32-byte pairs so the eight rows of one transposing read hit distinct banks.
+//  * Block means: sum_j p_j mean_{b(j)} = sum_b L_b mean_b with L_b the row sum of p over the
+//    listed keys of block b.  The blocks of a tile are mapped to slots of a window of 32
+//    consecutive blocks; one more FP8 MFMA with a 0/1 slot indicator as A accumulates L (32 slots
+//    x 32 rows) next to O.  When a key falls past the window, the window is flushed into O with
+//    v_mfma_f32_32x32x16_bf16 (A = mean / scale of the window's blocks, read channel-major from
+//    HBM; B = L rounded to bf16) and the row sum takes sum_b L_b.  Keys are ascending, so the
+//    window only moves forward.
+#include <stdlib.h>
+
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sattn {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+
+constexpr int VS_BLOCK = VSMOOTH_BLOCK;   // tokens per V-Smooth mean block
+constexpr int F8_BK = 64;       // listed keys per tile
+constexpr int F8_WIN = 32;      // mean blocks per slot window
+
+// ---------------------------------------------------------------------------------------------
+// V-Smooth quantisation
+// ---------------------------------------------------------------------------------------------
+
+// Nearest bf16 of a double, ties to even: truncate to fp32 with round-to-odd (sticky bit), then
+// round fp32 -> bf16 to nearest even; round-to-odd with 16 spare bits makes the double rounding exact.
+__device__ inline uint32_t bf16_bits_rne_f64(double x) {
+  const float t = __double2float_rz(x);
+  uint32_t u = __float_as_uint(t);
+  if ((double)t != x) u |= 1u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Per (head, block): bf16 block means (exact fp64 sum of the bf16 tokens, divided by the token
+// count) and the per-channel max |v - mean| of the block.
+template <int D>
+__global__ __launch_bounds__(256) void k_vs_stats(const uint16_t* __restrict__ v, int Nk, int NB,
+                                                  uint16_t* __restrict__ mean_ws, float* __restrict__ bmax_ws) {
+  constexpr int TPC = 256 / D;            // threads per channel
+  constexpr int TOK = VS_BLOCK / TPC;     // tokens per thread
+  __shared__ double part[256];
+  __shared__ float pmax[256];
+  const int blk = (int)(blockIdx.x % (uint32_t)NB);
+  const size_t bh = blockIdx.x / (uint32_t)NB;
+  const int d = threadIdx.x % D, pi = threadIdx.x / D;
+  const int nb0 = blk * VS_BLOCK;
+  const int ntok = min(VS_BLOCK, Nk - nb0);
+  const uint16_t* vb = v + (bh * Nk + nb0) * D + d;
+  float x[TOK];
+#pragma unroll
+  for (int i = 0; i < TOK; ++i) {
+    const int t = pi * TOK + i;
+    x[i] = t < ntok ? bf16_bits_to_float(vb[(size_t)t * D]) : 0.0f;
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < TOK; ++i) s += (double)x[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int p = 0; p < TPC; ++p) tot += part[p * D + d];
+  const uint32_t mb = bf16_bits_rne_f64(tot / (double)ntok);
+  const float mf = bf16_bits_to_float(mb);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < TOK; ++i)
+    if (pi * TOK + i < ntok) m = fmaxf(m, fabsf(x[i] - mf));
+  pmax[threadIdx.x] = m;
+  __syncthreads();
+  if (pi == 0) {
+    float a = pmax[d];
+#pragma unroll
+    for (int p = 1; p < TPC; ++p) a = fmaxf(a, pmax[p * D + d]);
+    mean_ws[(bh * NB + blk) * D + d] = (uint16_t)mb;
+    bmax_ws[(bh * NB + blk) * D + d] = a;
+  }
+}
+
+// Per head: channel scale 2^e, the smallest power of two with 448 * 2^e >= max |residual|.
+template <int D>
+__global__ __launch_bounds__(D) void k_vs_scale(const float* __restrict__ bmax_ws, int NB, float* __restrict__ vscale) {
+  const size_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  float a = 0.0f;
+  for (int b = 0; b < NB; ++b) a = fmaxf(a, bmax_ws[(bh * NB + b) * D + d]);
+  int e = 0;
+  if (a > 0.0f) {
+    int x;
+    const float f = frexpf(a, &x);        // a = f 2^x, 0.5 <= f < 1; 448 = 0.875 * 2^9
+    e = f <= 0.875f ? x - 9 : x - 8;
+  }
+  vscale[bh * D + d] = ldexpf(1.0f, e);
+}
+
+// Per (head, block): E4M3 codes of (v - mean) / scale and the channel-major scaled means.
+template <int D>
+__global__ __launch_bounds__(256) void k_vs_codes(const uint16_t* __restrict__ v, int Nk, int NB, int nbp,
+                                                  const uint16_t* __restrict__ mean_ws,
+                                                  const float* __restrict__ vscale, uint8_t* __restrict__ codes,
+                                                  uint16_t* __restrict__ vmean) {
+  constexpr int CH = D / 8;               // 16-byte chunks of a bf16 row
+  __shared__ float mu[D], inv[D];
+  const int blk = (int)(blockIdx.x % (uint32_t)NB);
+  const size_t bh = blockIdx.x / (uint32_t)NB;
+  const int nb0 = blk * VS_BLOCK;
+  const int ntok = min(VS_BLOCK, Nk - nb0);
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    const float m = bf16_bits_to_float(mean_ws[(bh * NB + blk) * D + d]);
+    const float is = 1.0f / vscale[bh * D + d];          // exact: the scale is a power of two
+    mu[d] = m;
+    inv[d] = is;
+    uint16_t* mrow = vmean + (bh * D + d) * (size_t)nbp;
+    mrow[blk] = (uint16_t)(__float_as_uint(m * is) >> 16);   // exact: bf16 times a power of two
+    if (blk == NB - 1)
+      for (int b = NB; b < nbp; ++b) mrow[b] = 0;
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < ntok * CH; w += 256) {
+    const int t = w / CH, ch = w % CH;
+    const size_t off = (bh * Nk + nb0 + t) * D + ch * 8;
+    const u32x4 raw = *(const u32x4*)(v + off);
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = (raw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      x[i] = (bf16_bits_to_float(bits) - mu[ch * 8 + i]) * inv[ch * 8 + i];
+    }
+    uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], (int)lo, true);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], (int)hi, true);
+    *(u32x2*)(codes + off) = u32x2{lo, hi};
+  }
+}
+
+int launch_vsmooth(const VsmoothArgs& a) {
+  const int NB = (a.Nk + VS_BLOCK - 1) / VS_BLOCK;
+  const int nbp = vsmooth_mean_stride(a.Nk);
+  const uint32_t BH = (uint32_t)a.B * (uint32_t)a.H;
+  uint16_t* mean_ws = (uint16_t*)a.workspace;
+  float* bmax_ws = (float*)((char*)a.workspace + vsmooth_mean_ws_bytes(a.B * a.H, a.Nk, a.D));
+  hipStream_t st = (hipStream_t)a.stream;
+  const uint16_t* v = (const uint16_t*)a.v;
+  if (a.D == 128) {
+    hipLaunchKernelGGL(k_vs_stats<128>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, mean_ws, bmax_ws);
+    hipLaunchKernelGGL(k_vs_scale<128>, dim3(BH), dim3(128), 0, st, bmax_ws, NB, a.vscale);
+    hipLaunchKernelGGL(k_vs_codes<128>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, nbp, mean_ws, a.vscale,
+                       a.codes, (uint16_t*)a.vmean);
+  } else {
+    hipLaunchKernelGGL(k_vs_stats<64>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, mean_ws, bmax_ws);
+    hipLaunchKernelGGL(k_vs_scale<64>, dim3(BH), dim3(64), 0, st, bmax_ws, NB, a.vscale);
+    hipLaunchKernelGGL(k_vs_codes<64>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, nbp, mean_ws, a.vscale,
+                       a.codes, (uint16_t*)a.vmean);
+  }
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Sparse forward with ExpCast bytes and the FP8 P.V product
+// ---------------------------------------------------------------------------------------------
+
+template <int D>
+struct F8Layout {
+  static constexpr int RB = 2 * D;                 // bytes per bf16 K row
+  static constexpr int NC = D / 8;                 // 16-byte chunks per K row
+  static constexpr int RPL = 1024 / RB;            // K rows filled by one 64-lane 16-byte load
+  static constexpr int KSETS = F8_BK / RPL;        // K loads per tile
+  static constexpr int NC8 = D / 16;               // 16-byte chunks per E4M3 V row
+  static constexpr int RPL8 = 1024 / D;            // V rows per load
+  static constexpr int VSETS = F8_BK / RPL8;       // V loads per tile
+  static constexpr int KBYTES = F8_BK * RB;
+  static constexpr int STAGE = KBYTES + F8_BK * D;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+  static constexpr int ROWDIV = 16 / NC;
+  // register budget: two waves per SIMD at D = 128 (O, both score halves, Q and the slot sums
+  // stay in VGPRs), three at D = 64
+  static constexpr int WAVES_PER_EU = D == 128 ? 2 : 3;
+  __device__ static inline int swz_k(int row) { return (row / ROWDIV) % NC; }
+  // 32-byte pair of a V row: the transposing read takes rows {0,1,2,3,8,9,10,11} (+4h, +16t) at one
+  // pair index; this XOR spreads them over all 64 banks
+  __device__ static inline int swz_v(int row) {
+    return D == 128 ? (((row >> 1) & 1) | (((row >> 3) & 1) << 1)) : ((row >> 3) & 1);
+  }
+};
+
+template <int N>
+using F8IC = std::integral_constant<int, N>;
+
+__device__ inline uint32_t expcast_byte(float s, float c1, float c0) {
+  const int y = (int)(__float_as_uint(__builtin_fmaf(s, c1, c0)) - 0x4B400000u);
+  return (uint32_t)min(max(y, 0), 126);
+}
+
+template <int D, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layout<D>::WAVES_PER_EU, F8Layout<D>::WAVES_PER_EU))) void attn_fwd_fp8(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint8_t* __restrict__ v8,
+    const float* __restrict__ vscale, const uint16_t* __restrict__ vmean, int nbp,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap, int Nq, int Nk, int group, int G,
+    float scale_log2, void* __restrict__ out, float* __restrict__ lse, uint32_t n_units) {
+  using L = F8Layout<D>;
+  constexpr int NKS = (L::KSETS + NW - 1) / NW;
+  constexpr int NVS = (L::VSETS + NW - 1) / NW;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t slot_lds[NW][F8_BK / 4];
+
+  const uint32_t unit = xcd_contiguous(blockIdx.x, n_units);
+  const int g = (int)(unit % (uint32_t)G);
+  const uint32_t bh = unit / (uint32_t)G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5;
+  const int ql = lane & 31;
+  const int r0 = g * group;
+  const int rows_in_group = min(group, Nq - r0);
+  const int wrow = wave * 32 + ql;
+  const bool row_valid = wrow < rows_in_group;
+
+  int c = counts[bh * (uint32_t)G + g];
+  c = c < 0 ? 0 : (c > cap ? cap : c);
+  const int nblk = (c + F8_BK - 1) / F8_BK;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8 + (size_t)bh * Nk * D, (uint32_t)Nk * D);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(vmean + (size_t)bh * D * nbp, (uint32_t)(D * nbp * 2));
+  const int32_t* ilist = idx + ((size_t)bh * G + g) * (size_t)cap;
+
+  bf16x8 qf[L::KSTEPS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (size_t)bh * Nq * D, (uint32_t)Nq * L::RB);
+    const uint32_t rowoff = row_valid ? (uint32_t)(r0 + wrow) * L::RB : (uint32_t)Nq * L::RB;
+#pragma unroll
+    for (int ks = 0; ks < L::KSTEPS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rq, rowoff + (uint32_t)(2 * ks + hi) * 16));
+  }
+  uint32_t koff[L::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < L::KSTEPS; ++ks) koff[ks] = ql * L::RB + 16 * ((2 * ks + hi) ^ L::swz_k(ql));
+  // transposing V reads: lane j of each 16-lane group supplies row vrow (+16 t) at byte 8 (j % 2)
+  // of the chunk 2 db + (group % 2)
+  const int j16 = lane & 15, g16 = lane >> 4;
+  const int e8 = j16 >> 1;
+  const int vrow = 8 * (e8 >> 2) + 4 * hi + (e8 & 3);
+  uint32_t voff[L::DBLK];
+#pragma unroll
+  for (int db = 0; db < L::DBLK; ++db)
+    voff[db] = vrow * D + 32 * (db ^ L::swz_v(vrow)) + 16 * (g16 & 1) + 8 * (j16 & 1);
+
+  const int krow_in = lane / L::NC, kpos = lane % L::NC;
+  const int vrow_in = lane / L::NC8, vpos = lane % L::NC8;
+  uint32_t kch[NKS], vch[NVS];
+#pragma unroll
+  for (int j = 0; j < NKS; ++j) {
+    const int row = (wave + j * NW) * L::RPL + krow_in;
+    kch[j] = 16u * (uint32_t)(kpos ^ L::swz_k(row));
+  }
+#pragma unroll
+  for (int j = 0; j < NVS; ++j) {
+    const int row = (wave + j * NW) * L::RPL8 + vrow_in;
+    vch[j] = 16u * (uint32_t)(2 * ((vpos >> 1) ^ L::swz_v(row)) + (vpos & 1));
+  }
+  int kkeys[NKS], vkeys[NVS];
+  auto fetch_keys = [&](int blk) {
+#pragma unroll
+    for (int j = 0; j < NKS; ++j) {
+      const int rs = wave + j * NW;
+      const int p = blk * F8_BK + rs * L::RPL + krow_in;
+      if (L::KSETS % NW == 0 || rs < L::KSETS) kkeys[j] = ilist[p < c ? p : c - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NVS; ++j) {
+      const int rs = wave + j * NW;
+      const int p = blk * F8_BK + rs * L::RPL8 + vrow_in;
+      if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = ilist[p < c ? p : c - 1];
+    }
+  };
+  auto issue = [&](char* stage) {
+#pragma unroll
+    for (int j = 0; j < NKS; ++j) {
+      const int rs = wave + j * NW;
+      if (L::KSETS % NW == 0 || rs < L::KSETS)
+        buffer_load_lds_x4(rk, stage + rs * L::RPL * L::RB, (uint32_t)kkeys[j] * L::RB + kch[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NVS; ++j) {
+      const int rs = wave + j * NW;
+      if (L::VSETS % NW == 0 || rs < L::VSETS)
+        buffer_load_lds_x4(rv, stage + L::KBYTES + rs * L::RPL8 * D, (uint32_t)vkeys[j] * D + vch[j]);
+    }
+  };
+  // the tile's listed key of this lane (lane = position in the tile), for the mean slots
+  auto tile_key = [&](int blk) {
+    const int p = blk * F8_BK + lane;
+    return p < c ? ilist[p] : -1;
+  };
+
+  f32x16 o[L::DBLK];
+#pragma unroll
+  for (int i = 0; i < L::DBLK; ++i) o[i] = f32x16{};
+  f32x16 lb = {};
+  float m8 = 0.0f, l_run = 0.0f;
+  int wbase = 0, wtop = 0;          // slot window [wbase, wbase + 32) of mean blocks; highest slot used
+  const float c1 = scale_log2 * 8.0f;
+  int tkey = 0;
+  const uint32_t* my_slots = slot_lds[wave];
+
+  // fold the window's block means into O: O += (mean / scale)^T L, row sums += sum of L
+  auto flush = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks == 1 && wtop < 16) break;
+      const u32x4 bw = {pack_bf16x2(lb[8 * ks], lb[8 * ks + 1]), pack_bf16x2(lb[8 * ks + 2], lb[8 * ks + 3]),
+                        pack_bf16x2(lb[8 * ks + 4], lb[8 * ks + 5]), pack_bf16x2(lb[8 * ks + 6], lb[8 * ks + 7])};
+#pragma unroll
+      for (int db = 0; db < L::DBLK; ++db) {
+        const uint32_t off = ((uint32_t)(32 * db + ql) * (uint32_t)nbp + (uint32_t)(wbase + 16 * ks + 4 * hi)) * 2u;
+        const u32x2 m0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off, 0, 0));
+        const u32x2 m1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off + 16, 0, 0));
+        const u32x4 aw = {m0[0], m0[1], m1[0], m1[1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), __builtin_bit_cast(bf16x8, bw),
+                                                       o[db], 0, 0, 0);
+      }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += lb[r];
+    l_run += s;
+    lb = f32x16{};
+  };
+
+  auto block = [&](auto st, int j) {
+    constexpr int ST = decltype(st)::value;
+    wait_vmcnt0();
+    __syncthreads();
+    const int key_here = tkey;
+    if (j + 1 < nblk) {
+      issue(smem + (1 - ST) * L::STAGE);
+      if (j + 2 < nblk) fetch_keys(j + 2);
+      tkey = tile_key(j + 1);
+    }
+    const char* sk = smem + ST * L::STAGE;
+    const char* sv = sk + L::KBYTES;
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int ks = 0; ks < L::KSTEPS; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(sk + koff[ks]);
+      const bf16x8 a1 = *(const bf16x8*)(sk + 32 * L::RB + koff[ks]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+    }
+    if (j == nblk - 1 && (c & (F8_BK - 1))) {
+      const int valid = c - j * F8_BK;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (kk >= valid) s0[r] = -INFINITY;
+        if (kk + 32 >= valid) s1[r] = -INFINITY;
+      }
+    }
+    // reference point of the row on the 1/8 grid
+    float bmax = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, fmaxf(s0[r], s1[r]));
+    bmax = pair_max(bmax) * scale_log2;
+    {
+      const bool move = j == 0 || bmax > m8 * 0.125f + 0.75f;
+      const float m8n = move ? ceilf(8.0f * bmax) : m8;
+      if (j > 0 && __builtin_amdgcn_ballot_w64(move) != 0) {
+        // In place (tied asm operands): a plain multiply under this branch makes the compiler keep
+        // a second copy of O.  The compiler does not pad hazards around inline asm, so the wait
+        // states are explicit: after the transcendental v_exp_f32 before its first VALU consumer,
+        // and after the last write before an MFMA may read these registers as its accumulator.
+        const float alpha = __builtin_amdgcn_exp2f((m8 - m8n) * 0.125f);
+        asm volatile("s_nop 4" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(lb[r]) : "v"(alpha));
+#pragma unroll
+        for (int i = 0; i < L::DBLK; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(o[i][r]) : "v"(alpha));
+        asm volatile("s_nop 7" ::: "memory");
+        l_run *= alpha;
+      }
+      m8 = m8n;
+    }
+    // ExpCast bytes, already in the B-operand order of the FP8 product
+    const float c0 = 12582912.0f + 120.0f - m8;
+    i32x8 pb;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int r = 4 * (w & 3);
+      const float x0 = w < 4 ? s0[r] : s1[r], x1 = w < 4 ? s0[r + 1] : s1[r + 1];
+      const float x2 = w < 4 ? s0[r + 2] : s1[r + 2], x3 = w < 4 ? s0[r + 3] : s1[r + 3];
+      pb[w] = (int)(expcast_byte(x0, c1, c0) | (expcast_byte(x1, c1, c0) << 8) | (expcast_byte(x2, c1, c0) << 16) |
+                    (expcast_byte(x3, c1, c0) << 24));
+    }
+#pragma unroll
+    for (int db = 0; db < L::DBLK; ++db) {
+      const char* p0 = sv + voff[db];
+      const i32x2v t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0));
+      const i32x2v t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 16 * D));
+      const i32x2v t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 32 * D));
+      const i32x2v t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 48 * D));
+      const i32x8 av = {t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, o[db], 0, 0, 0, 0, 0, 0);
+    }
+    // block-mean slots of this tile's keys; a key past the window flushes it and starts the next
+    const int kb = key_here >= 0 ? (key_here >> 7) : 0x7FFFFFFF;
+    if (j == 0) wbase = __builtin_amdgcn_readfirstlane(kb) & ~3;
+    uint8_t* slot_bytes = (uint8_t*)slot_lds[wave];
+    while (true) {
+      const int sl = kb - wbase;
+      const bool in_win = sl >= 0 && sl < F8_WIN;
+      slot_bytes[lane] = (uint8_t)(in_win ? sl : 0xFF);
+      const uint64_t inm = __builtin_amdgcn_ballot_w64(in_win);
+      if (inm != 0) {
+        const int top = 63 - __builtin_clzll(inm);
+        wtop = max(wtop, __builtin_amdgcn_readlane(sl, top));
+        const uint32_t pat = (uint32_t)ql * 0x01010101u;
+        i32x8 ind;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const uint32_t x = my_slots[2 * w + hi] ^ pat;
+          const uint32_t t = ((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x | 0x7F7F7F7Fu;
+          const uint32_t z = ~t & 0x80808080u;             // 0x80 in the bytes equal to this lane's slot
+          ind[w] = (int)((z >> 1) - (z >> 4));              // 0x38 (E4M3 1.0) there, 0 elsewhere
+        }
+        lb = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ind, pb, lb, 0, 0, 0, 0, 0, 0);
+      }
+      const uint64_t past = __builtin_amdgcn_ballot_w64(kb != 0x7FFFFFFF && sl >= F8_WIN);
+      if (past == 0) break;
+      flush();
+      wbase = __builtin_amdgcn_readlane(kb, __builtin_ctzll(past)) & ~3;
+      wtop = 0;
+    }
+  };
+
+  if (nblk > 0) {
+    fetch_keys(0);
+    issue(smem);
+    if (nblk > 1) fetch_keys(1);
+    tkey = tile_key(0);
+  }
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    block(F8IC<0>{}, j);
+    block(F8IC<1>{}, j + 1);
+  }
+  if (j < nblk) block(F8IC<0>{}, j);
+  if (nblk > 0) flush();
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (row_valid) {
+    const size_t orow = ((size_t)bh * Nq + r0 + wrow) * D;
+    const float* sc = vscale + (size_t)bh * D;
+#pragma unroll
+    for (int db = 0; db < L::DBLK; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * hi;
+        const f32x4 s = *(const f32x4*)(sc + d0);
+        const float x0 = o[db][4 * i] * s[0] * inv, x1 = o[db][4 * i + 1] * s[1] * inv;
+        const float x2 = o[db][4 * i + 2] * s[2] * inv, x3 = o[db][4 * i + 3] * s[3] * inv;
+        if (OUT_F32) *(f32x4*)((float*)out + orow + d0) = f32x4{x0, x1, x2, x3};
+        else *(u32x2*)((uint16_t*)out + orow + d0) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      }
+    if (lse != nullptr && hi == 0)
+      lse[(size_t)bh * Nq + r0 + wrow] =
+          l_tot > 0.0f ? (m8 * 0.125f - 8.0f + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+template <int D, int NW>
+static int launch_fp8_t(const Fp8FwdArgs& a) {
+  const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
+  const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  const int nbp = vsmooth_mean_stride(a.Nk);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (a.out_f32)
+    hipLaunchKernelGGL((attn_fwd_fp8<D, NW, true>), dim3(n_units), dim3(NW * 64), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap,
+                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+  else
+    hipLaunchKernelGGL((attn_fwd_fp8<D, NW, false>), dim3(n_units), dim3(NW * 64), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap,
+                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+static int launch_fp8_d(const Fp8FwdArgs& a) {
+  const int waves = (a.group + 31) / 32;
+  if (waves <= 2) return launch_fp8_t<D, 2>(a);
+  if (waves <= 4) return launch_fp8_t<D, 4>(a);
+  if (waves <= 6) return launch_fp8_t<D, 6>(a);
+  return launch_fp8_t<D, 8>(a);
+}
+
+int launch_fp8_fwd(const Fp8FwdArgs& a) { return a.D == 64 ? launch_fp8_d<64>(a) : launch_fp8_d<128>(a); }
+
+}  // namespace sattn

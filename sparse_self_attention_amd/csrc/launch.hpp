@@ -85,6 +85,46 @@ struct ColsumArgs {
 };
 int launch_colsum_scores(const ColsumArgs& a);
 
+// V-Smooth quantisation of V (fp8_attn.hip): E4M3 codes [B,H,Nk,D], power-of-two channel scales
+// [B,H,D] and channel-major scaled block means [B,H,D,vsmooth_mean_stride(Nk)] (bf16 mean / scale).
+constexpr int VSMOOTH_BLOCK = 128;
+inline int vsmooth_blocks(int Nk) { return (Nk + VSMOOTH_BLOCK - 1) / VSMOOTH_BLOCK; }
+inline int vsmooth_mean_stride(int Nk) { return (vsmooth_blocks(Nk) + 3) & ~3; }
+inline size_t vsmooth_mean_ws_bytes(int BH, int Nk, int D) {
+  return ((size_t)BH * vsmooth_blocks(Nk) * D * 2 + 255) & ~(size_t)255;
+}
+inline size_t vsmooth_workspace_bytes(int BH, int Nk, int D) {
+  return vsmooth_mean_ws_bytes(BH, Nk, D) + (((size_t)BH * vsmooth_blocks(Nk) * D * 4 + 255) & ~(size_t)255);
+}
+struct VsmoothArgs {
+  const void* v;
+  int B, H, Nk, D;
+  uint8_t* codes;
+  float* vscale;
+  void* vmean;
+  void* workspace;
+  void* stream;
+};
+int launch_vsmooth(const VsmoothArgs& a);
+
+struct Fp8FwdArgs {
+  const void* q;
+  const void* k;
+  const uint8_t* codes;
+  const float* vscale;
+  const void* vmean;
+  const int32_t* idx;
+  const int32_t* counts;
+  int cap;
+  int B, H, Nq, Nk, D, group;
+  float scale;
+  void* out;
+  bool out_f32;
+  float* lse;
+  void* stream;
+};
+int launch_fp8_fwd(const Fp8FwdArgs& a);
+
 int launch_permute_tokens(const void* src, void* dst, const int32_t* perm, int BH, int N, int D, int inverse,
                           void* stream);
 

@@ -33,7 +33,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"sattn_mask", "sattn_forward", "attn_forward", "sattn_mask_workspace_bytes", "sattn_cached_mask",
-            "sattn_colsum_mask", "sattn_delta_forward",
+            "sattn_colsum_mask", "sattn_delta_forward", "sattn_vsmooth_quantize", "sattn_fp8_forward",
+            "sattn_vsmooth_workspace_bytes", "sattn_vsmooth_mean_stride",
             "sattn_strerror", "sattn_last_error", "sattn_voxel_permutation", "sattn_permute_tokens"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sattn.h but not exported"
@@ -151,6 +152,54 @@ DELTA_CASES = [
 @pytest.mark.parametrize("kw,code", DELTA_CASES, ids=[str(c[0]) for c in DELTA_CASES])
 def test_delta_forward_validation(lib, kw, code):
     assert dlt(lib, **kw) == code
+
+
+def vsq(lib, v=FAKE, B=1, H=1, Nk=300, D=128, codes=FAKE, vscale=FAKE, vmean=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sattn_vsmooth_quantize(v, B, H, Nk, D, codes, vscale, vmean, ws, ws_bytes, P(0))
+
+
+VSMOOTH_CASES = [
+    (dict(v=P(0)), ERR_NULL), (dict(codes=P(0)), ERR_NULL), (dict(vmean=P(0)), ERR_NULL), (dict(Nk=0), ERR_SHAPE),
+    (dict(D=96), ERR_UNSUPPORTED), (dict(codes=P(4104)), ERR_ARG), (dict(vscale=P(4100)), ERR_ARG),
+    (dict(vmean=P(4098)), ERR_ARG), (dict(ws=P(0)), ERR_WORKSPACE), (dict(ws_bytes=64), ERR_WORKSPACE),
+    (dict(ws=P(4096 + 128)), ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,code", VSMOOTH_CASES, ids=[str(c[0]) for c in VSMOOTH_CASES])
+def test_vsmooth_validation(lib, kw, code):
+    assert vsq(lib, **kw) == code
+    assert lib.sattn_last_error()
+
+
+def f8f(lib, q=FAKE, k=FAKE, codes=FAKE, vscale=FAKE, vmean=FAKE, idx=FAKE, counts=FAKE, cap=64, B=1, H=1, Nq=128,
+        Nk=128, D=128, group=128, scale=0.1, out=FAKE, out_dtype=1, lse=P(0)):
+    return lib.sattn_fp8_forward(q, k, codes, vscale, vmean, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out,
+                                 out_dtype, lse, P(0))
+
+
+FP8_CASES = [
+    (dict(codes=P(0)), ERR_NULL), (dict(vscale=P(0)), ERR_NULL), (dict(vmean=P(0)), ERR_NULL), (dict(out=P(0)), ERR_NULL),
+    (dict(B=0), ERR_SHAPE), (dict(D=32), ERR_UNSUPPORTED), (dict(group=24), ERR_UNSUPPORTED),
+    (dict(scale=0.0), ERR_ARG), (dict(cap=0), ERR_ARG), (dict(out_dtype=3), ERR_ARG),
+    (dict(codes=P(4104)), ERR_ARG), (dict(vscale=P(4100)), ERR_ARG), (dict(vmean=P(4104)), ERR_ARG),
+    (dict(lse=P(4098)), ERR_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", FP8_CASES, ids=[str(c[0]) for c in FP8_CASES])
+def test_fp8_forward_validation(lib, kw, code):
+    assert f8f(lib, **kw) == code
+    assert lib.sattn_last_error()
+
+
+def test_vsmooth_sizes(lib):
+    assert lib.sattn_vsmooth_mean_stride(70200) == 552 and lib.sattn_vsmooth_mean_stride(128) == 4
+    assert lib.sattn_vsmooth_mean_stride(129) == 4 and lib.sattn_vsmooth_mean_stride(513) == 8
+    assert lib.sattn_vsmooth_mean_stride(0) == 0
+    # bf16 means and fp32 block maxima of every (head, block, channel), each part 256-byte aligned
+    assert lib.sattn_vsmooth_workspace_bytes(1, 24, 70200, 128) == 24 * 549 * 128 * 6
+    assert lib.sattn_vsmooth_workspace_bytes(1, 1, 10, 96) == 0
 
 
 def test_dense_validation(lib):

@@ -1,0 +1,196 @@
+"""GPU parity of the FP8 value path: V-Smooth quantisation (sattn_vsmooth_quantize, bit-exact against
+the oracle) and the ExpCast / E4M3 P.V forward (sattn_fp8_forward) against the fp64 oracle fed the
+oracle's own codes, scales and block means."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_lse, check_out, f64, scale_of, to_device_bf16, workload
+from synth import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def sattn():
+    import sparse_self_attention_amd as s
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert os.path.exists(s.library_path()), "libsattn.so is not built"
+    return s
+
+
+def _bits(rng, shape, std=1.0, offset=None):
+    x = rng.standard_normal(shape) * std
+    if offset is not None:
+        x = x + offset
+    return inputs.f32_to_bf16_bits(x.astype(np.float32))
+
+
+def _stride(nk):
+    return 4 * (-(-(-(-nk // 128)) // 4))
+
+
+def _to_device_quant(codes, scale, mean, nk):
+    """The oracle's (codes, scale, mean [B,H,NB,D]) in the library's layout: mean / scale channel-major,
+    padded with zeros to the stride (exact: the scale is a power of two)."""
+    B, H, NB, D = mean.shape
+    m = np.zeros((B, H, D, _stride(nk)), dtype=np.float32)
+    m[:, :, :, :NB] = np.transpose(mean / scale[:, :, None, :], (0, 1, 3, 2))
+    mb = inputs.f32_to_bf16_bits(m)
+    assert np.array_equal(inputs.bf16_bits_to_f32(mb), m), "scaled means must be exact in bf16"
+    return (torch.from_numpy(np.ascontiguousarray(codes)).to(DEV), torch.from_numpy(scale.astype(np.float32)).to(DEV),
+            to_device_bf16(mb, DEV))
+
+
+def _check_quant(sattn, vb, what):
+    """GPU quantisation of V against the oracle, bit for bit."""
+    v = to_device_bf16(vb, DEV)
+    codes, vscale, vmean = sattn.vsmooth_quantize(v)
+    torch.cuda.synchronize()
+    rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
+    gc = codes.cpu().numpy()
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{what}: {len(bad)} codes differ, first {bad[0]} gpu {gc[tuple(bad[0])]:#x} " \
+                          f"oracle {rc[tuple(bad[0])]:#x}"
+    gs = vscale.cpu().numpy().astype(np.float64)
+    assert np.array_equal(gs, rs), f"{what}: channel scales differ"
+    gm = vmean.float().cpu().numpy().astype(np.float64)
+    NB = rm.shape[2]
+    assert np.array_equal(gm[:, :, :, :NB] * gs[:, :, :, None], np.transpose(rm, (0, 1, 3, 2))), f"{what}: means differ"
+    assert not gm[:, :, :, NB:].any(), f"{what}: mean padding not zero"
+    return rc, rs, rm
+
+
+# (D, Nk, offsets of the 128-token blocks)
+QUANT_CASES = [(128, 300, True), (64, 1000, True), (128, 128, False), (64, 77, False), (128, 4097, True)]
+
+
+@pytest.mark.parametrize("D,Nk,offsets", QUANT_CASES)
+def test_vsmooth_bit_exact(sattn, D, Nk, offsets):
+    rng = np.random.default_rng(D + Nk)
+    off = None
+    if offsets:
+        off = np.repeat(rng.uniform(-4, 4, size=(2, -(-Nk // 128), 1)), 128, axis=1)[:, :Nk][None]
+    vb = _bits(rng, (1, 2, Nk, D), 1.0, off)
+    vb[0, 1, :, 3] = inputs.f32_to_bf16_bits(np.float32(0.625))     # a constant channel: scale 1, codes 0
+    _check_quant(sattn, vb, f"D={D} Nk={Nk}")
+
+
+def _lists(rng, B, H, G, Nk, counts, kind):
+    cap = max(1, int(counts.max()))
+    if kind == "random":
+        return inputs.random_index_lists(rng, B, H, G, Nk, counts, cap)
+    idx = np.full((B, H, G, cap), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                c = int(counts[b, h, g])
+                if kind == "spread":           # one key per 128-token block: 64 blocks in every tile
+                    base = rng.integers(0, 128, size=c)
+                    keys = np.minimum(np.arange(c) * 128 + base, Nk - 1)
+                    keys = np.unique(keys)
+                    counts[b, h, g] = keys.size
+                elif kind == "jumps":          # runs of 20 keys with gaps of ~40 blocks between runs
+                    starts = np.cumsum(rng.integers(4000, 6000, size=-(-c // 20)))
+                    keys = np.unique(np.minimum((starts[:, None] + np.arange(20)[None]).ravel()[:c], Nk - 1))
+                    counts[b, h, g] = keys.size
+                else:                          # one block
+                    keys = np.sort(rng.choice(128, size=min(c, 128), replace=False)) + 128 * (g % max(1, Nk // 128))
+                    keys = keys[keys < Nk]
+                    counts[b, h, g] = keys.size
+                idx[b, h, g, :keys.size] = keys
+    return idx
+
+
+def _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0, zero_group=True, out_bf16=False):
+    B, H = 1, 2
+    G = -(-Nq // group)
+    qb = _bits(rng, (B, H, Nq, D), q_std)
+    kb = _bits(rng, (B, H, Nk, D))
+    off = np.repeat(rng.uniform(-2, 2, size=(H, -(-Nk // 128), 1)), 128, axis=1)[:, :Nk][None]
+    vb = _bits(rng, (B, H, Nk, D), 1.0, off)
+    counts = rng.integers(1, cmax + 1, size=(B, H, G)).astype(np.int32)
+    counts[0, 0, 0] = cmax
+    if zero_group and G > 1:
+        counts[0, 1, G - 1] = 0
+    idx = _lists(rng, B, H, G, Nk, counts, kind)
+    rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
+    scale = scale_of(D)
+    ro, rl = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale)
+    codes, vscale, vmean = _to_device_quant(rc, rs, rm, Nk)
+    q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
+    check_out(out.cpu().numpy(), ro, what)
+    check_lse(lse.cpu().numpy(), rl, what)
+    if zero_group and G > 1:
+        r = slice((G - 1) * group, Nq)
+        assert not out[0, 1, r].any().item() and torch.isneginf(lse[0, 1, r]).all().item()
+    if out_bf16:
+        ob, _ = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, group, out_dtype=torch.bfloat16)
+        assert torch.equal(ob, out.to(torch.bfloat16)), f"{what}: bf16 output is not the rounded fp32 output"
+
+
+# (D, group, Nq, Nk, max count, list kind)
+FWD_CASES = [
+    (128, 128, 300, 3000, 700, "random"),      # several tiles, ragged last tile and group
+    (64, 64, 200, 5000, 1500, "random"),       # many windows of 32 blocks
+    (128, 192, 400, 9000, 70, "spread"),       # every tile spans 64 blocks (several window passes)
+    (64, 256, 300, 70000, 200, "jumps"),       # windows far apart
+    (128, 16, 50, 1000, 128, "one"),           # one block per list, one wave
+    (128, 96, 100, 200, 200, "random"),        # Nk below two blocks, every key listed
+    (64, 128, 128, 77, 77, "random"),          # one ragged V block
+]
+
+
+@pytest.mark.parametrize("D,group,Nq,Nk,cmax,kind", FWD_CASES)
+def test_fp8_forward(sattn, D, group, Nq, Nk, cmax, kind):
+    rng = np.random.default_rng(D * 7 + group + Nq + Nk)
+    _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, out_bf16=(D == 128 and group == 128))
+
+
+def test_fp8_forward_large_logits(sattn):
+    """Scores spread over tens of log2 units: the reference point moves, bytes clamp at 0."""
+    rng = np.random.default_rng(5)
+    _run_case(sattn, rng, 128, 128, 256, 4000, 900, "random", q_std=6.0)
+
+
+def test_fp8_full_size_sampled(sattn):
+    """The long-video workload in the benchmark's launch configuration (all 24 heads, 20 % lists): the
+    GPU quantisation of head 0 bit-exact; head 0's forward on the oracle's quantisation and seeded
+    random lists, checked on sampled groups."""
+    w, (qb, kb, vb) = workload("long_70200")
+    rng = np.random.default_rng(70200)
+    rc, rs, rm = _check_quant(sattn, vb[:, :1], "long_70200 head 0")
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    codes, vscale, vmean = sattn.vsmooth_quantize(v)
+    c0, s0, m0 = _to_device_quant(rc, rs, rm, w.n_k)
+    codes[:, :1].copy_(c0)
+    vscale[:, :1].copy_(s0)
+    vmean[:, :1].copy_(m0)
+    counts = np.full((1, w.heads, w.groups), w.topk, dtype=np.int32)
+    units = [(0, 0, g) for g in (0, 1, w.groups // 2, w.groups - 1)]
+    idx = np.zeros((1, w.heads, w.groups, w.topk), dtype=np.int32)
+    idx[:] = np.arange(w.topk, dtype=np.int32) * (w.n_k // w.topk)     # fills the heads not checked
+    for (_, _, g) in units:
+        idx[0, 0, g] = np.sort(rng.choice(w.n_k, size=w.topk, replace=False))
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, w.group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    scale = scale_of(w.dim)
+    for (_, _, g) in units:
+        r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
+        ui = idx[:, :1, g:g + 1]
+        uc = counts[:, :1, g:g + 1]
+        ro, rl = oracle.fp8_attention_ref(f64(qb[:, :1, r]), f64(kb[:, :1]), rc, rs, rm, ui, uc, w.group, scale)
+        check_out(out_h[:, :1, r], ro, f"long_70200 fp8 g={g}")
+        check_lse(lse_h[:, :1, r], rl, f"long_70200 fp8 g={g}")
