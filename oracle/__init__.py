@@ -23,9 +23,9 @@ Readings of passages that the pages leave open:
   * the Chipmunk sparse delta uses the full-softmax form the review asks for:
     probabilities with a stale lse, no renormalisation over the selected keys;
   * the FP8 value path takes bf16 block means, power-of-two channel scales, a
-    reference point on the 1/8 grid of log2 units moved only when a block's max
-    exceeds it by more than 3/4, and ExpCast bytes with the probability scaled by
-    2^8 (bias 120 instead of 56); oracle/fp8.py states each.
+    reference point on the 1/8 grid of log2 units moved by whole log2 units only
+    when a byte would pass the largest finite code, and ExpCast bytes with the
+    probability scaled by 2^8 (bias 120 instead of 56); oracle/fp8.py states each.
 """
 from .attention import dense_attention_ref, sparse_attention_ref, sparse_attention_probs_ref  # noqa: F401
 from .mask import (group_mean_ref, group_scores_ref, topk_select_ref, thresh_select_ref,  # noqa: F401

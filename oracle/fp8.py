@@ -20,12 +20,13 @@ Readings where the summary is silent (each is what the GPU path computes as well
   * probabilities: the online softmax runs over blocks of 64 listed keys in list order
     (LongLive DiT blog, "Online Softmax").  The reference point m of a row lies on the 1/8
     grid of log2 units so that 8 x + bias is one multiply-add of the raw score plus an
-    integer: m = ceil8(block max) on the first block, and a later block moves it to
-    ceil8(its max) only when its max exceeds m + 3/4 (below that its largest byte is at
-    most 126, the largest finite code); the weights gathered so far are then scaled by
-    2^(m_old - m_new).  The byte is round-half-even(8 (x - m) + 120), set to 0 below 0:
-    the bias 56 with the probability scaled by 2^8, so the row's largest weight sits near
-    256 and only weights below 2^-14 of it fall into the subnormal codes;
+    integer: m = ceil8(block max) on the first block; a later block moves it only when one
+    of its bytes would pass 126, the largest finite code (block max > m + 13/16), and then
+    by the smallest whole number of log2 units that brings the block max to or below it,
+    so the weights gathered so far are scaled by an exact power of two.  The byte is
+    round-half-even(8 (x - m) + 120), set to 0 below 0: the bias 56 with the probability
+    scaled by 2^8, so the row's largest weight sits near 256 and only weights below 2^-14
+    of it fall into the subnormal codes;
   * the row sum adds the decoded probabilities; out = sum_j p_j (s v8_j + mean_b(j)) / l;
     lse = ln(l 2^(m - 8)).
 Where a decision is integer (a code, a byte), the oracle takes it on the values the
@@ -44,7 +45,7 @@ import numpy as np
 FP8_BLOCK = 64          # listed keys per online-softmax block
 VS_BLOCK = 128          # tokens per V-Smooth mean block
 EXPCAST_BIAS = 56.0 + 64.0      # E4M3 exponent bias 7 (x 8) plus the 2^8 scale
-RESCALE_SLACK = 0.75            # a block max up to m + 3/4 keeps the reference point
+RESCALE_SLACK = 13.0 / 16.0     # a block max past m + 13/16 would give a byte above 126
 
 
 def e4m3_decode_table() -> np.ndarray:
@@ -141,9 +142,9 @@ def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale
     """out, lse of the FP8 value path over per-group key lists.
 
     For each group and its listed keys J (list order), blocks of `block` keys: s2 = scale q.k log2 e
-    (fp64); the row's reference point m8 = 8 m (an integer) is set from the first block's max and
-    moved only when a block's max exceeds m + 3/4; P-bytes = expcast(s2 - m); weights gathered earlier
-    are scaled by 2^(m_old - m_new); O += decode(P) @ Vhat[J], l += sum decode(P), with
+    (fp64); the row's reference point m8 = 8 m (an integer) is ceil(8 max) of the first block and moves
+    by 8 ceil(max - m) only when a block's max exceeds m + 13/16; P-bytes = expcast(s2 - m); weights
+    gathered earlier are scaled by 2^(m_old - m_new); O += decode(P) @ Vhat[J], l += sum decode(P), with
     Vhat = scale * E4M3(code) + block mean.  out = O / l; lse = ln(l) + (m - 8) ln 2.
     c = 0 gives out = 0, lse = -inf.
     """
@@ -176,7 +177,7 @@ def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale
                         m8 = np.ceil(8.0 * bm)
                     else:
                         move = bm > m8 / 8.0 + RESCALE_SLACK
-                        m8new = np.where(move, np.ceil(8.0 * bm), m8)
+                        m8new = np.where(move, m8 + 8.0 * np.ceil(bm - m8 / 8.0), m8)
                         alpha = np.exp2((m8 - m8new) / 8.0)
                         o *= alpha[:, None]
                         l *= alpha

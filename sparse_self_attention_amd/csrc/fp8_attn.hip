@@ -9,34 +9,39 @@
 //    mean / scale are exact.
 //  * ExpCast: the probability byte is one multiply-add of the raw score plus an integer,
 //    round-half-even(8 (x - m) + 120) clamped to [0, 126], where x is the score in log2 units and
-//    m the row's reference point.  m lies on the 1/8 grid: set by the first block of 64 listed keys
-//    as ceil8(block max), moved to ceil8(block max) only when a block's max exceeds m + 3/4 (the
-//    largest byte then stays <= 126), the earlier sums scaled by 2^(m_old - m_new).  The bias
+//    m the row's reference point.  m lies on the 1/8 grid: ceil8(max) of the first block of 64
+//    listed keys; a later block moves it only when one of its bytes would pass 126, and then by the
+//    smallest whole number of log2 units that brings the block max to or below it.  The bias
 //    120 = 56 + 64 carries the probability scaled by 2^8.
 //
 // Mapping onto CDNA4
 // ------------------
 //  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32).  Tiles of 64
-//    listed keys: K rows (bf16) and V rows (E4M3, D bytes) are gathered from HBM into LDS with
-//    16-byte buffer-load-to-LDS instructions, double-buffered.
+//    listed keys: K rows (bf16), V rows (E4M3, D bytes) and one 32-byte slot row per key are
+//    gathered into LDS with 16-byte buffer-load-to-LDS instructions, double-buffered.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 as in the bf16 path (two 32-key halves); each lane
-//    owns one query row and 32 of the 64 keys, so the block max is in-lane plus one lane-pair
-//    exchange, and the 32 probability bytes of a lane are exactly the B operand of
-//    v_mfma_f32_32x32x64_f8f6f4 for its row: no register shuffle between the two products.
+//    owns one query row and 32 of the 64 keys, and its 32 probability bytes are exactly the B
+//    operand of v_mfma_f32_32x32x64_f8f6f4 for its row: no shuffle between the two products.
 //    Byte b = 16 s + r of lane (row, h) holds key 32 s + 8 (r / 4) + 4 h + r % 4.
 //  * The byte: y = fma(score, 8 scale log2e, 1.5 * 2^23 + 120 - 8m) puts round-half-even(8 (x - m)
-//    + 120) in the low mantissa bits, and an integer subtract and clamp give the byte.  One fp32
-//    operation per probability instead of an exp, a conversion and a sum.
+//    + 120) in the low mantissa bits; an integer clamp to [0, 127] and v_perm_b32 pack four bytes
+//    per word.  A byte of 127 flags the rare block whose reference point must move.
+//  * Moves are whole powers of two, so O is never rescaled: O, the slot sums and the row sums stay
+//    in the frame of the row's first reference point and each product takes its row's 2^(m - m0)
+//    through the per-lane E8M0 B scale of v_mfma_scale_f32_32x32x64_f8f6f4 (exact).  The scale is
+//    capped at 2^90 (the fp32 sums stay finite): a row whose max grows by more than 90 log2 units past
+//    its first block weighs its later blocks as if it had grown by 90.
 //  * O^T += V8^T P^T: A = the V codes read from LDS with ds_read_b64_tr_b8 (the gfx950 transposing
 //    byte read), four 8-byte reads per 64-key tile and 32 output dims.  Rows are XOR-swizzled in
 //    32-byte pairs so the eight rows of one transposing read hit distinct banks.
-//  * Block means: sum_j p_j mean_{b(j)} = sum_b L_b mean_b with L_b the row sum of p over the
-//    listed keys of block b.  The blocks of a tile are mapped to slots of a window of 32
-//    consecutive blocks; one more FP8 MFMA with a 0/1 slot indicator as A accumulates L (32 slots
-//    x 32 rows) next to O.  When a key falls past the window, the window is flushed into O with
-//    v_mfma_f32_32x32x16_bf16 (A = mean / scale of the window's blocks, read channel-major from
-//    HBM; B = L rounded to bf16) and the row sum takes sum_b L_b.  Keys are ascending, so the
-//    window only moves forward.
+//  * Block means: sum_j p_j mean_{b(j)} = sum_b L_b mean_b with L_b the row sum of p over the listed
+//    keys of block b.  Blocks are grouped in aligned windows of 32; key j's slot is b(j) mod 32, and
+//    its slot row (0x38 = E4M3 1.0 at byte b(j) mod 32) is copied from a 1 KB table by the same DMA,
+//    so one more FP8 MFMA with A = the transposed slot rows accumulates L (32 slots x 32 rows) next
+//    to O with no VALU work.  When the list passes into the next window, L is folded into O with
+//    v_mfma_f32_32x32x16_bf16 (A = mean / scale of the window's blocks, channel-major in HBM; B = L
+//    rounded to bf16) and the row sums take sum_b L_b.  A tile that straddles windows masks P per
+//    window for the slot product.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -52,6 +57,7 @@ typedef int i32x2v __attribute__((ext_vector_type(2)));
 constexpr int VS_BLOCK = VSMOOTH_BLOCK;   // tokens per V-Smooth mean block
 constexpr int F8_BK = 64;       // listed keys per tile
 constexpr int F8_WIN = 32;      // mean blocks per slot window
+constexpr int F8_MAX_GROWTH = 90;   // log2 units a row max may grow past its first block
 
 // ---------------------------------------------------------------------------------------------
 // V-Smooth quantisation
@@ -206,7 +212,9 @@ struct F8Layout {
   static constexpr int RPL8 = 1024 / D;            // V rows per load
   static constexpr int VSETS = F8_BK / RPL8;       // V loads per tile
   static constexpr int KBYTES = F8_BK * RB;
-  static constexpr int STAGE = KBYTES + F8_BK * D;
+  static constexpr int VBYTES = F8_BK * D;
+  static constexpr int IBYTES = F8_BK * 32;        // one 32-byte slot row per key
+  static constexpr int STAGE = KBYTES + VBYTES + IBYTES;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   static constexpr int ROWDIV = 16 / NC;
@@ -224,13 +232,44 @@ struct F8Layout {
 template <int N>
 using F8IC = std::integral_constant<int, N>;
 
-__device__ inline uint32_t expcast_byte(float s, float c1, float c0) {
-  const int y = (int)(__float_as_uint(__builtin_fmaf(s, c1, c0)) - 0x4B400000u);
-  return (uint32_t)min(max(y, 0), 126);
+// Slot rows: row m holds E4M3 1.0 (0x38) at byte m and zeros elsewhere.
+struct OneHotTable {
+  uint8_t b[F8_WIN * 32];
+};
+constexpr OneHotTable make_onehot() {
+  OneHotTable t{};
+  for (int m = 0; m < F8_WIN; ++m) t.b[m * 32 + m] = 0x38;
+  return t;
+}
+__device__ __attribute__((aligned(256))) const OneHotTable k_onehot = make_onehot();
+
+// Stored position of slot row r of a tile: rows 8..11 and 12..15 of every 16 trade places, so the
+// eight rows one transposing read touches ({0..3, 8..11} + 4h) cover all 64 banks.  An involution.
+__device__ inline int ind_pos(int r) { return r ^ ((r & 8) >> 1); }
+
+// ExpCast: the float bits clamped so that the low byte is the code, 0..127 (0x4B400000 = 1.5 * 2^23
+// holds 0; 127 flags a byte past the largest finite code)
+__device__ inline uint32_t expcast_bits(float s, float c1, float c0) {
+  const int y = (int)__float_as_uint(__builtin_fmaf(s, c1, c0));
+  return (uint32_t)min(max(y, 0x4B400000), 0x4B40007F);
+}
+// low bytes of four words -> one word (v_perm_b32: selector bytes 0-3 pick from the second operand,
+// 4-7 from the first, 0x0C gives 0)
+__device__ inline uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+// byte masks of the keys [lo, hi) of a tile for the four keys 8 w + 4 h + 0..3 of dword w
+__device__ inline uint32_t key_byte_mask(uint64_t m64, int w, int h) {
+  const uint32_t nib = (uint32_t)(m64 >> (8 * w + 4 * h)) & 0xFu;
+  const uint32_t spread = (nib * 0x00204081u) & 0x01010101u;
+  return (spread << 8) - spread;
 }
 
 template <int D, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layout<D>::WAVES_PER_EU, F8Layout<D>::WAVES_PER_EU))) void attn_fwd_fp8(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layout<D>::WAVES_PER_EU,
+                                                                         F8Layout<D>::WAVES_PER_EU))) void attn_fwd_fp8(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint8_t* __restrict__ v8,
     const float* __restrict__ vscale, const uint16_t* __restrict__ vmean, int nbp,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap, int Nq, int Nk, int group, int G,
@@ -238,8 +277,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   using L = F8Layout<D>;
   constexpr int NKS = (L::KSETS + NW - 1) / NW;
   constexpr int NVS = (L::VSETS + NW - 1) / NW;
+  constexpr int ISETS = L::IBYTES / 1024;          // slot-row loads per tile (2)
+  static_assert(NW >= ISETS, "one slot-row load per wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
-  __shared__ __attribute__((aligned(16))) uint32_t slot_lds[NW][F8_BK / 4];
 
   const uint32_t unit = xcd_contiguous(blockIdx.x, n_units);
   const int g = (int)(unit % (uint32_t)G);
@@ -259,6 +299,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8 + (size_t)bh * Nk * D, (uint32_t)Nk * D);
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(vmean + (size_t)bh * D * nbp, (uint32_t)(D * nbp * 2));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(k_onehot.b, (uint32_t)sizeof(k_onehot.b));
   const int32_t* ilist = idx + ((size_t)bh * G + g) * (size_t)cap;
 
   bf16x8 qf[L::KSTEPS];
@@ -269,33 +310,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     for (int ks = 0; ks < L::KSTEPS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rq, rowoff + (uint32_t)(2 * ks + hi) * 16));
   }
-  uint32_t koff[L::KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < L::KSTEPS; ++ks) koff[ks] = ql * L::RB + 16 * ((2 * ks + hi) ^ L::swz_k(ql));
-  // transposing V reads: lane j of each 16-lane group supplies row vrow (+16 t) at byte 8 (j % 2)
-  // of the chunk 2 db + (group % 2)
+  // per-lane offsets are recomputed where used (a few integer operations) rather than held in VGPRs
+  const uint32_t kbase = ql * L::RB;
+  const int kswz = L::swz_k(ql);
+  auto koff = [&](int ks) { return kbase + 16u * (uint32_t)((2 * ks + hi) ^ kswz); };
+  // transposing reads: lane j of each 16-lane group supplies row vrow (+16 t) at byte 8 (j % 2) of
+  // the 16-byte chunk 2 db + (group % 2) (V codes) or (group % 2) (slot rows)
   const int j16 = lane & 15, g16 = lane >> 4;
   const int e8 = j16 >> 1;
   const int vrow = 8 * (e8 >> 2) + 4 * hi + (e8 & 3);
-  uint32_t voff[L::DBLK];
-#pragma unroll
-  for (int db = 0; db < L::DBLK; ++db)
-    voff[db] = vrow * D + 32 * (db ^ L::swz_v(vrow)) + 16 * (g16 & 1) + 8 * (j16 & 1);
+  const uint32_t vbase = vrow * D + 16 * (g16 & 1) + 8 * (j16 & 1);
+  const int vswz = L::swz_v(vrow);
+  auto voff = [&](int db) { return vbase + 32u * (uint32_t)(db ^ vswz); };
+  const uint32_t ioff = L::KBYTES + L::VBYTES + ind_pos(vrow) * 32 + 16 * (g16 & 1) + 8 * (j16 & 1);
 
   const int krow_in = lane / L::NC, kpos = lane % L::NC;
   const int vrow_in = lane / L::NC8, vpos = lane % L::NC8;
-  uint32_t kch[NKS], vch[NVS];
-#pragma unroll
-  for (int j = 0; j < NKS; ++j) {
+  auto kch = [&](int j) {
     const int row = (wave + j * NW) * L::RPL + krow_in;
-    kch[j] = 16u * (uint32_t)(kpos ^ L::swz_k(row));
-  }
-#pragma unroll
-  for (int j = 0; j < NVS; ++j) {
+    return 16u * (uint32_t)(kpos ^ L::swz_k(row));
+  };
+  auto vch = [&](int j) {
     const int row = (wave + j * NW) * L::RPL8 + vrow_in;
-    vch[j] = 16u * (uint32_t)(2 * ((vpos >> 1) ^ L::swz_v(row)) + (vpos & 1));
-  }
-  int kkeys[NKS], vkeys[NVS];
+    return 16u * (uint32_t)(2 * ((vpos >> 1) ^ L::swz_v(row)) + (vpos & 1));
+  };
+  // slot-row load of this wave (waves 0 and 1): LDS position 32 wave + lane / 2 holds key row
+  // ind_pos(position), chunk lane % 2
+  const int irow = ind_pos(32 * wave + (lane >> 1));
+  int kkeys[NKS], vkeys[NVS], ikey = 0;
   auto fetch_keys = [&](int blk) {
 #pragma unroll
     for (int j = 0; j < NKS; ++j) {
@@ -309,22 +351,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
       const int p = blk * F8_BK + rs * L::RPL8 + vrow_in;
       if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = ilist[p < c ? p : c - 1];
     }
+    if (wave < ISETS) {
+      const int p = blk * F8_BK + irow;
+      ikey = ilist[p < c ? p : c - 1];
+    }
   };
   auto issue = [&](char* stage) {
 #pragma unroll
     for (int j = 0; j < NKS; ++j) {
       const int rs = wave + j * NW;
       if (L::KSETS % NW == 0 || rs < L::KSETS)
-        buffer_load_lds_x4(rk, stage + rs * L::RPL * L::RB, (uint32_t)kkeys[j] * L::RB + kch[j]);
+        buffer_load_lds_x4(rk, stage + rs * L::RPL * L::RB, (uint32_t)kkeys[j] * L::RB + kch(j));
     }
 #pragma unroll
     for (int j = 0; j < NVS; ++j) {
       const int rs = wave + j * NW;
       if (L::VSETS % NW == 0 || rs < L::VSETS)
-        buffer_load_lds_x4(rv, stage + L::KBYTES + rs * L::RPL8 * D, (uint32_t)vkeys[j] * D + vch[j]);
+        buffer_load_lds_x4(rv, stage + L::KBYTES + rs * L::RPL8 * D, (uint32_t)vkeys[j] * D + vch(j));
     }
+    if (wave < ISETS)
+      buffer_load_lds_x4(ro, stage + L::KBYTES + L::VBYTES + wave * 1024,
+                         (uint32_t)((ikey >> 7) & (F8_WIN - 1)) * 32u + 16u * (uint32_t)(lane & 1));
   };
-  // the tile's listed key of this lane (lane = position in the tile), for the mean slots
+  // the tile's listed key of this lane (lane = position in the tile), for the mean windows
   auto tile_key = [&](int blk) {
     const int p = blk * F8_BK + lane;
     return p < c ? ilist[p] : -1;
@@ -334,22 +383,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
 #pragma unroll
   for (int i = 0; i < L::DBLK; ++i) o[i] = f32x16{};
   f32x16 lb = {};
-  float m8 = 0.0f, l_run = 0.0f;
-  int wbase = 0, wtop = 0;          // slot window [wbase, wbase + 32) of mean blocks; highest slot used
+  float m8 = 0.0f, mbase8 = 0.0f, l_run = 0.0f;
+  int escale = 127;                 // E8M0 B scale of this row: 2^(m - m0)
+  int win = 0, slot_lo = F8_WIN, slot_hi = -1;   // current window of 32 blocks; slots it has used
   const float c1 = scale_log2 * 8.0f;
   int tkey = 0;
-  const uint32_t* my_slots = slot_lds[wave];
 
   // fold the window's block means into O: O += (mean / scale)^T L, row sums += sum of L
   auto flush = [&]() {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if (ks == 1 && wtop < 16) break;
+      if ((ks == 0 && slot_lo >= 16) || (ks == 1 && slot_hi < 16)) continue;
       const u32x4 bw = {pack_bf16x2(lb[8 * ks], lb[8 * ks + 1]), pack_bf16x2(lb[8 * ks + 2], lb[8 * ks + 3]),
                         pack_bf16x2(lb[8 * ks + 4], lb[8 * ks + 5]), pack_bf16x2(lb[8 * ks + 6], lb[8 * ks + 7])};
 #pragma unroll
       for (int db = 0; db < L::DBLK; ++db) {
-        const uint32_t off = ((uint32_t)(32 * db + ql) * (uint32_t)nbp + (uint32_t)(wbase + 16 * ks + 4 * hi)) * 2u;
+        const uint32_t off =
+            ((uint32_t)(32 * db + ql) * (uint32_t)nbp + (uint32_t)(F8_WIN * win + 16 * ks + 4 * hi)) * 2u;
         const u32x2 m0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off, 0, 0));
         const u32x2 m1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, off + 16, 0, 0));
         const u32x4 aw = {m0[0], m0[1], m1[0], m1[1]};
@@ -362,10 +412,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     for (int r = 0; r < 16; ++r) s += lb[r];
     l_run += s;
     lb = f32x16{};
+    slot_lo = F8_WIN;
+    slot_hi = -1;
   };
 
-  auto block = [&](auto st, int j) {
-    constexpr int ST = decltype(st)::value;
+  auto block = [&](int j) {
+    const int ST = j & 1;
     wait_vmcnt0();
     __syncthreads();
     const int key_here = tkey;
@@ -379,13 +431,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     f32x16 s0 = {}, s1 = {};
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(sk + koff[ks]);
-      const bf16x8 a1 = *(const bf16x8*)(sk + 32 * L::RB + koff[ks]);
+      const bf16x8 a0 = *(const bf16x8*)(sk + koff(ks));
+      const bf16x8 a1 = *(const bf16x8*)(sk + 32 * L::RB + koff(ks));
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
     }
-    if (j == nblk - 1 && (c & (F8_BK - 1))) {
-      const int valid = c - j * F8_BK;
+    const int valid = min(F8_BK, c - j * F8_BK);
+    if (valid < F8_BK) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -393,81 +445,88 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
         if (kk + 32 >= valid) s1[r] = -INFINITY;
       }
     }
-    // reference point of the row on the 1/8 grid
-    float bmax = fmaxf(s0[0], s1[0]);
+    auto block_max = [&]() {
+      float bmax = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, fmaxf(s0[r], s1[r]));
-    bmax = pair_max(bmax) * scale_log2;
-    {
-      const bool move = j == 0 || bmax > m8 * 0.125f + 0.75f;
-      const float m8n = move ? ceilf(8.0f * bmax) : m8;
-      if (j > 0 && __builtin_amdgcn_ballot_w64(move) != 0) {
-        // In place (tied asm operands): a plain multiply under this branch makes the compiler keep
-        // a second copy of O.  The compiler does not pad hazards around inline asm, so the wait
-        // states are explicit: after the transcendental v_exp_f32 before its first VALU consumer,
-        // and after the last write before an MFMA may read these registers as its accumulator.
-        const float alpha = __builtin_amdgcn_exp2f((m8 - m8n) * 0.125f);
-        asm volatile("s_nop 4" ::: "memory");
-#pragma unroll
-        for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(lb[r]) : "v"(alpha));
-#pragma unroll
-        for (int i = 0; i < L::DBLK; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(o[i][r]) : "v"(alpha));
-        asm volatile("s_nop 7" ::: "memory");
-        l_run *= alpha;
-      }
-      m8 = m8n;
-    }
-    // ExpCast bytes, already in the B-operand order of the FP8 product
-    const float c0 = 12582912.0f + 120.0f - m8;
+      for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, fmaxf(s0[r], s1[r]));
+      return pair_max(bmax) * scale_log2;
+    };
+    // ExpCast bytes, already in the B-operand order of the FP8 products
     i32x8 pb;
+    auto make_bytes = [&]() {
+      const float c0 = 12582912.0f + 120.0f - m8;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int r = 4 * (w & 3);
-      const float x0 = w < 4 ? s0[r] : s1[r], x1 = w < 4 ? s0[r + 1] : s1[r + 1];
-      const float x2 = w < 4 ? s0[r + 2] : s1[r + 2], x3 = w < 4 ? s0[r + 3] : s1[r + 3];
-      pb[w] = (int)(expcast_byte(x0, c1, c0) | (expcast_byte(x1, c1, c0) << 8) | (expcast_byte(x2, c1, c0) << 16) |
-                    (expcast_byte(x3, c1, c0) << 24));
+      for (int w = 0; w < 8; ++w) {
+        const int r = 4 * (w & 3);
+        const float x0 = w < 4 ? s0[r] : s1[r], x1 = w < 4 ? s0[r + 1] : s1[r + 1];
+        const float x2 = w < 4 ? s0[r + 2] : s1[r + 2], x3 = w < 4 ? s0[r + 3] : s1[r + 3];
+        pb[w] = (int)pack4(expcast_bits(x0, c1, c0), expcast_bits(x1, c1, c0), expcast_bits(x2, c1, c0),
+                           expcast_bits(x3, c1, c0));
+      }
+    };
+    if (j == 0) {
+      m8 = ceilf(8.0f * block_max());
+      mbase8 = m8;
+      make_bytes();
+    } else {
+      make_bytes();
+      uint32_t acc = 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) acc |= (uint32_t)pb[w] + 0x01010101u;
+      // a byte of 127 (past the largest finite code) in either lane of the row moves the row's point
+      const uint64_t mv = __builtin_amdgcn_ballot_w64((acc & 0x80808080u) != 0);
+      if (mv != 0) {
+        const bool move = ((mv >> ql) | (mv >> (ql + 32))) & 1u;
+        const float bmax = block_max();
+        if (move) m8 += 8.0f * ceilf(bmax - m8 * 0.125f);
+        make_bytes();
+        // the frame holds 2^90 of growth past the first block (fp32 sums of up to 2^11 tiles stay finite)
+        escale = 127 + min((int)((m8 - mbase8) * 0.125f), F8_MAX_GROWTH);
+      }
     }
 #pragma unroll
     for (int db = 0; db < L::DBLK; ++db) {
-      const char* p0 = sv + voff[db];
+      const char* p0 = sv + voff(db);
       const i32x2v t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0));
       const i32x2v t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 16 * D));
       const i32x2v t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 32 * D));
       const i32x2v t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 48 * D));
       const i32x8 av = {t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
-      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, o[db], 0, 0, 0, 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, o[db], 0, 0, 0, 127, 0, escale);
     }
-    // block-mean slots of this tile's keys; a key past the window flushes it and starts the next
-    const int kb = key_here >= 0 ? (key_here >> 7) : 0x7FFFFFFF;
-    if (j == 0) wbase = __builtin_amdgcn_readfirstlane(kb) & ~3;
-    uint8_t* slot_bytes = (uint8_t*)slot_lds[wave];
+    i32x8 ia;
+    {
+      const char* p0 = sk + ioff;
+      const i32x2v t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0));
+      const i32x2v t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 512));
+      const i32x2v t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 1024));
+      const i32x2v t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 1536));
+      ia = i32x8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+    }
+    // block-mean slot sums: this tile's keys by aligned window of 32 blocks (key >> 12)
+    const int kw = key_here >= 0 ? (key_here >> 12) : 0x7FFFFFFF;
+    const int kslot = (key_here >> 7) & (F8_WIN - 1);
+    if (j == 0) win = __builtin_amdgcn_readfirstlane(kw);
+    // keys of windows <= win form a prefix of the tile; a tile that straddles windows masks P to
+    // each window's keys in turn (the common tile takes one pass with P unmasked)
+    int lo = 0;
     while (true) {
-      const int sl = kb - wbase;
-      const bool in_win = sl >= 0 && sl < F8_WIN;
-      slot_bytes[lane] = (uint8_t)(in_win ? sl : 0xFF);
-      const uint64_t inm = __builtin_amdgcn_ballot_w64(in_win);
-      if (inm != 0) {
-        const int top = 63 - __builtin_clzll(inm);
-        wtop = max(wtop, __builtin_amdgcn_readlane(sl, top));
-        const uint32_t pat = (uint32_t)ql * 0x01010101u;
-        i32x8 ind;
+      const int nhi = __builtin_popcountll(__builtin_amdgcn_ballot_w64(kw <= win));
+      if (nhi > lo) {
+        i32x8 pm = pb;
+        if (lo > 0 || nhi < valid) {
+          const uint64_t m64 = (nhi >= 64 ? ~0ull : ((1ull << nhi) - 1ull)) & ~((1ull << lo) - 1ull);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const uint32_t x = my_slots[2 * w + hi] ^ pat;
-          const uint32_t t = ((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x | 0x7F7F7F7Fu;
-          const uint32_t z = ~t & 0x80808080u;             // 0x80 in the bytes equal to this lane's slot
-          ind[w] = (int)((z >> 1) - (z >> 4));              // 0x38 (E4M3 1.0) there, 0 elsewhere
+          for (int w = 0; w < 8; ++w) pm[w] = (int)((uint32_t)pb[w] & key_byte_mask(m64, w, hi));
         }
-        lb = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ind, pb, lb, 0, 0, 0, 0, 0, 0);
+        lb = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ia, pm, lb, 0, 0, 0, 127, 0, escale);
+        slot_lo = min(slot_lo, __builtin_amdgcn_readlane(kslot, lo));
+        slot_hi = max(slot_hi, __builtin_amdgcn_readlane(kslot, nhi - 1));
       }
-      const uint64_t past = __builtin_amdgcn_ballot_w64(kb != 0x7FFFFFFF && sl >= F8_WIN);
-      if (past == 0) break;
+      if (nhi >= valid) break;
       flush();
-      wbase = __builtin_amdgcn_readlane(kb, __builtin_ctzll(past)) & ~3;
-      wtop = 0;
+      win = __builtin_amdgcn_readlane(kw, nhi);
+      lo = nhi;
     }
   };
 
@@ -477,12 +536,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     if (nblk > 1) fetch_keys(1);
     tkey = tile_key(0);
   }
-  int j = 0;
-  for (; j + 1 < nblk; j += 2) {
-    block(F8IC<0>{}, j);
-    block(F8IC<1>{}, j + 1);
-  }
-  if (j < nblk) block(F8IC<0>{}, j);
+  for (int j = 0; j < nblk; ++j) block(j);
   if (nblk > 0) flush();
 
   const float l_tot = pair_sum(l_run);
@@ -503,7 +557,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
       }
     if (lse != nullptr && hi == 0)
       lse[(size_t)bh * Nq + r0 + wrow] =
-          l_tot > 0.0f ? (m8 * 0.125f - 8.0f + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+          l_tot > 0.0f ? (mbase8 * 0.125f - 8.0f + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
 }
 

@@ -582,14 +582,17 @@ def check_vsmooth(vsmooth, decode_table):
 
 def _fp8_brute_row(s2, vrows, t):
     """One row by explicit loops: the reference point m8 / 8 on the 1/8 grid, set by the first block of
-    64 and moved to ceil8(block max) only past m + 3/4, weights E4M3(round(8 s2 - m8 + 120))."""
+    64; a later block whose bytes under the current point would include one above 126 moves it up by
+    whole log2 units until the block max is at or below it; weights E4M3(round(8 s2 - m8 + 120))."""
     m8, w, moves = None, {}, 0
     for j0 in range(0, len(s2), 64):
         bm = max(s2[j0:j0 + 64])
         if m8 is None:
             m8 = math.ceil(8 * bm)
-        elif bm > m8 / 8 + 0.75:
-            new = math.ceil(8 * bm)
+        elif max(round(8 * x - m8 + 120) for x in s2[j0:j0 + 64]) > 126:
+            new = m8
+            while bm > new / 8:
+                new += 8
             for jj in w:
                 w[jj] *= 2.0 ** ((m8 - new) / 8)
             m8, moves = new, moves + 1
@@ -643,8 +646,8 @@ def check_fp8_attention(vsmooth, fp8_attn, decode_table, dequant):
             exact_lse = max(s2) * ln2 + math.log(ex.sum())
             assert abs(lse[0, h, i] - exact_lse) <= 0.15 * ln2
     # scores rising along the list: by 1/5 per block of 64 (the reference point stays, bytes climb past
-    # 120) and by 5/4 per block (it moves every block and the earlier weights are carried over)
-    for slope, moves in ((0.2 / 64, 0), (1.25 / 64, 3)):
+    # 120) and by 2 per block (it moves every block and the earlier weights are carried over)
+    for slope, moves in ((0.2 / 64, 0), (2.0 / 64, 3)):
         kr = np.zeros((1, 1, 256, 4))
         kr[0, 0, :, 0] = np.arange(256) * slope * ln2 - 3.0
         kr[0, 0, :, 1] = rng.standard_normal(256) * 0.05

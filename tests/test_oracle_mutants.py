@@ -107,7 +107,8 @@ FP8_MUTANTS = [
     ("ExpCast bias without the 2^8 scale", "EXPCAST_BIAS = 56.0 + 64.0", "EXPCAST_BIAS = 56.0 + 56.0"),
     ("ExpCast truncates", "b = np.rint(y)", "b = np.floor(y)"),
     ("reference point off the 1/8 grid", "m8 = np.ceil(8.0 * bm)\n", "m8 = 8.0 * bm\n"),
-    ("reference point kept past saturation", "RESCALE_SLACK = 0.75", "RESCALE_SLACK = 2.0"),
+    ("reference point kept past saturation", "RESCALE_SLACK = 13.0 / 16.0", "RESCALE_SLACK = 2.0"),
+    ("reference point moved by a fraction", "m8 + 8.0 * np.ceil(bm - m8 / 8.0)", "np.ceil(8.0 * bm)"),
     ("earlier blocks not rescaled", "o *= alpha[:, None]", "o *= 1.0"),
     ("block mean not restored", "return _DEC[codes] * scale[:, :, None, :] + mean[:, :, np.arange(N) // VS_BLOCK, :]",
      "return _DEC[codes] * scale[:, :, None, :]"),
