@@ -25,7 +25,10 @@ Readings of passages that the pages leave open:
   * the FP8 value path takes bf16 block means, power-of-two channel scales, a
     reference point on the 1/8 grid of log2 units moved by whole log2 units only
     when a byte would pass the largest finite code, and ExpCast bytes with the
-    probability scaled by 2^8 (bias 120 instead of 56); oracle/fp8.py states each.
+    probability scaled by 2^8 (bias 120 instead of 56); oracle/fp8.py states each;
+  * the 4-bit QK^T path quantises queries and keys to MXFP4 (E2M1, blocks of 32 along the head
+    dimension, power-of-two scales, block maximum to 6); oracle/fp4.py explains why FourOverSix's
+    max-to-4 candidate never wins with power-of-two scales.
 """
 from .attention import dense_attention_ref, sparse_attention_ref, sparse_attention_probs_ref  # noqa: F401
 from .mask import (group_mean_ref, group_scores_ref, topk_select_ref, thresh_select_ref,  # noqa: F401
@@ -34,3 +37,5 @@ from .cached import (row_lse_ref, slice_max_logprob_ref, cached_mask_ref, colsum
                      colsum_mask_ref, delta_fresh_ref, delta_forward_ref)
 from .fp8 import (e4m3_decode_table, e4m3_encode, bf16_round, channel_scale_exponent,  # noqa: F401
                   vsmooth_quantize_ref, expcast_byte, dequantize_ref, fp8_attention_ref)
+from .fp4 import (e2m1_decode_table, e2m1_encode, mx4_quantize_ref, mx4_dequantize_ref,  # noqa: F401
+                  fp4_attention_ref)

@@ -677,3 +677,88 @@ def check_fp8_attention(vsmooth, fp8_attn, decode_table, dequant):
     out1, lse1 = fp8_attn(q, k, codes, vs, vm, idx1, cnt1, M, scale)
     assert np.allclose(out1[0, 0], vhat[0, 0, 200], atol=1e-12)
     assert not out1[0, 1, :M].any() and np.all(np.isneginf(lse1[0, 1, :M]))
+
+
+def check_e2m1(decode_table, encode):
+    """E2M1 code values (OCP microscaling specification: 1 sign, 2 exponent bits with bias 1, 1 mantissa
+    bit; code 1 is the subnormal 0.5) and nearest-even encoding against brute force, ties included."""
+    t = decode_table()
+    assert list(t[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert all(t[c | 8] == -t[c] for c in range(8))
+    for c in range(8):
+        e, m = (c >> 1) & 3, c & 1
+        assert t[c] == ((m / 2.0) if e == 0 else (1 + m / 2.0) * 2.0 ** (e - 1))
+    rng = np.random.default_rng(61)
+    x = np.concatenate([rng.uniform(-7, 7, 2000), [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -5.0, 6.0, 9.0]])
+    got = encode(x)
+    for xi, gi in zip(x, got):
+        xs = min(max(xi, -6.0), 6.0)
+        d = np.abs(t - xs)
+        best = [c for c in range(16) if d[c] == d.min() and (c & 8) == (8 if xs < 0 else 0) or (d[c] == d.min() and t[c] == 0)]
+        if len(best) > 1:
+            best = [c for c in best if c % 2 == 0] or best
+        assert t[gi] == t[best[0]], (xi, gi, best)
+    assert list(encode([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])) == [0, 2, 2, 4, 4, 6, 6]
+
+
+def check_mx4(quantize, dequantize, decode_table):
+    """MXFP4 blocks against brute force: the scale is the smallest power of two that brings the block
+    maximum to 6 or below, every code is the nearest E2M1 value of x / scale, zero blocks stay zero;
+    rule 4over6 equals rule 6 (with power-of-two scales the max-to-4 grid is a subset), while on each
+    block the max-to-4 candidate's error is checked directly to be no smaller."""
+    t = decode_table()
+    rng = np.random.default_rng(67)
+    x = rng.standard_normal((3, 5, 64)) * np.exp(rng.uniform(-4, 4, (3, 5, 1)))
+    x[0, 0, :32] = 0.0
+    x[1, 1, 32:] = np.linspace(4.0, 5.9, 32) * 2.0 ** -3         # clustered near the maximum
+    codes, exps = quantize(x, rule="6")
+    assert codes.shape == x.shape and exps.shape == (3, 5, 2)
+    xb, cb = x.reshape(-1, 32), codes.reshape(-1, 32)
+    for r, e in enumerate(exps.reshape(-1)):
+        blk = xb[r]
+        amax = np.abs(blk).max()
+        if amax == 0:
+            assert e == 0 and not cb[r].any()
+            continue
+        assert 6.0 * 2.0 ** e >= amax and 6.0 * 2.0 ** (e - 1) < amax, (r, e, amax)
+        for xi, ci in zip(blk, cb[r]):
+            d = np.abs(t * 2.0 ** e - xi)
+            assert d[ci] == d.min(), (r, xi, ci)
+        # the max-to-4 candidate 2^(e + 1) (when it differs) is never better
+        e4 = e if 4.0 * 2.0 ** e >= amax else e + 1
+        err6 = math.fsum((t[cb[r]] * 2.0 ** e - blk) ** 2)
+        y = blk / 2.0 ** e4
+        c4 = [int(np.argmin(np.abs(t - min(max(v, -6.0), 6.0)))) for v in y]
+        err4 = math.fsum((t[c4] * 2.0 ** e4 - blk) ** 2)
+        assert err6 <= err4 + 1e-300
+    c2, e2 = quantize(x, rule="4over6")
+    assert np.array_equal(c2, codes) and np.array_equal(e2, exps)
+    deq = dequantize(codes, exps)
+    assert np.all(np.abs(deq - x) <= np.repeat(2.0 ** exps, 32, axis=-1) * 1.0 + 1e-12)   # half the widest gap (2)
+
+
+def check_fp4_attention(quantize, fp4_attn, fp8_attn, vsmooth, decode_table):
+    """Queries and keys that are exactly MXFP4-representable (grid values times a power of two per block,
+    with the block maximum at 4 or 6) quantise without error, so the 4-bit path equals the FP8 path on the
+    original vectors; and rounding matters: perturbed keys move the scores by at most the quantisation
+    error (Cauchy-Schwarz on the dequantised vectors)."""
+    t = decode_table()
+    rng = np.random.default_rng(71)
+    B, H, Nq, Nk, D, M = 1, 1, 12, 90, 64, 4
+
+    def grid(shape):
+        v = t[rng.integers(0, 16, size=shape + (D,))]
+        v[..., ::32] = 6.0 * rng.choice([-1, 1], size=shape + (D // 32,))     # pin every block maximum to 6
+        return v * np.repeat(2.0 ** rng.integers(-3, 3, size=shape + (D // 32,)), 32, axis=-1)
+
+    q, k = grid((B, H, Nq)), grid((B, H, Nk))
+    qc, qe = quantize(q)
+    kc, ke = quantize(k)
+    assert np.array_equal(t[qc] * np.repeat(2.0 ** qe, 32, axis=-1), q)
+    v = rng.standard_normal((B, H, Nk, D))
+    vc, vs, vm = vsmooth(v)
+    G = -(-Nq // M)
+    idx, cnt = _random_lists(rng, B, H, G, Nk, 70)
+    o4, l4 = fp4_attn(qc, qe, kc, ke, vc, vs, vm, idx, cnt, M, 0.125)
+    o8, l8 = fp8_attn(q, k, vc, vs, vm, idx, cnt, M, 0.125)
+    assert np.array_equal(o4, o8) and np.array_equal(l4, l8)

@@ -134,6 +134,29 @@ def test_fp8_mutant_is_caught(name, old, new):
     assert _caught(checks), f"no pin catches the planted mistake: {name}"
 
 
+FP4_MUTANTS = [
+    ("E2M1 level 3 read as 2.5", "_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)",
+     "_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0)"),
+    ("ties away from even", "((dhi == dlo) & (hi % 2 == 0))", "(dhi == dlo)"),
+    ("maximum scaled to 4", "e6 = smallest_exponent(amax, 6.0)", "e6 = smallest_exponent(amax, 4.0)"),
+    ("scale one binade too small", "    e = math.ceil(math.log2(amax / top)) - 1\n    while top * 2.0 ** e < amax:",
+     "    e = math.ceil(math.log2(amax / top)) - 2\n    while top * 2.0 ** e < amax / 2:"),
+    ("blocks of 16", "MX_BLOCK = 32", "MX_BLOCK = 16"),
+    ("keys not dequantised", "mx4_dequantize_ref(k_codes, k_exps), v_codes", "k_codes.astype(float), v_codes"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", FP4_MUTANTS, ids=[m[0] for m in FP4_MUTANTS])
+def test_fp4_mutant_is_caught(name, old, new):
+    m = _mutant("oracle.fp4", old, new)
+    import oracle
+    checks = [lambda: pins.check_e2m1(m.e2m1_decode_table, m.e2m1_encode),
+              lambda: pins.check_mx4(m.mx4_quantize_ref, m.mx4_dequantize_ref, m.e2m1_decode_table),
+              lambda: pins.check_fp4_attention(m.mx4_quantize_ref, m.fp4_attention_ref, oracle.fp8_attention_ref,
+                                               oracle.vsmooth_quantize_ref, m.e2m1_decode_table)]
+    assert _caught(checks), f"no pin catches the planted mistake: {name}"
+
+
 @pytest.mark.parametrize("name,old,new", DELTA_MUTANTS, ids=[m[0] for m in DELTA_MUTANTS])
 def test_delta_mutant_is_caught(name, old, new):
     m = _mutant("oracle.cached", old, new)
