@@ -230,6 +230,35 @@ int sattn_fp8_forward(const void* q, const void* k, const uint8_t* codes, const 
                       void* out, int out_dtype, float* lse, void* stream);
 
 /*
+ * 4-bit QK^T (LongLive DiT blog, section "1. NVFP4": E2M1 codes with a shared scale per block,
+ * applied inside the block-scaled matrix product).  On gfx950 the format is MXFP4 (OCP microscaling):
+ * blocks of 32 elements along the head dimension with power-of-two (E8M0) scales.
+ *
+ * sattn_mx4_quantize - per row of x and block of 32: scale 2^e with the smallest e such that
+ * 6 * 2^e >= max |x| (e >= -127; e = 0 for a zero block), codes = nearest E2M1 of x / 2^e (ties to
+ * the even code).  (FourOverSix's max-to-4 alternative never has the smaller error with power-of-two
+ * scales, so max-to-6 is the rule.)
+ *   x       bf16 [B,H,N,D], 16-byte aligned (queries or keys).
+ *   codes   out: uint8 [B,H,N,D/2], two codes a byte (even element in the low nibble), 16-byte aligned.
+ *   scales  out: uint8 [B,H,N,4], byte b = e + 127 of block b (D/32 blocks; at D = 64 bytes 2 and 3 are
+ *           127), 4-byte aligned.
+ * Errors: NULL pointers, D not 64/128, bad sizes or alignment.
+ */
+int sattn_mx4_quantize(const void* x, int B, int H, int N, int D, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * sattn_fp4_forward - sattn_fp8_forward with the scores from the MXFP4 queries and keys:
+ * s = scale * sum_b 2^(eq_b + ek_b) E2M1(q_b) . E2M1(k_b), on v_mfma_scale_f32_32x32x64_f8f6f4 in
+ * FP4 x FP4.  q4, q_scales, k4, k_scales: sattn_mx4_quantize of Q and K; everything else as
+ * sattn_fp8_forward.  Errors: as sattn_fp8_forward; q4 and k4 16-byte, the scales 4-byte aligned.
+ */
+int sattn_fp4_forward(const uint8_t* q4, const uint8_t* q_scales, const uint8_t* k4, const uint8_t* k_scales,
+                      const uint8_t* codes, const float* vscale, const void* vmean,
+                      const int32_t* idx, const int32_t* counts, int cap,
+                      int B, int H, int Nq, int Nk, int D, int group, float scale,
+                      void* out, int out_dtype, float* lse, void* stream);
+
+/*
  * sattn_voxel_permutation - host-side token order that makes every run of vt*vy*vx tokens one
  * spatio-temporal voxel of a (T, Hg, Wg) raster grid.
  * Chipmunk review, "What carries the argument" and Fig. 2 caption (voxel reordering so that

@@ -20,8 +20,9 @@ even code; |x / 2^e| <= 6 by construction); under rule "4over6" the candidate wi
 squared errors sum (2^e E2M1(code) - x)^2 over the block wins, the max-to-6 one on a tie.  With
 power-of-two scales the max-to-4 candidate, when it differs, is 2^(e+1), whose grid below 6 * 2^e is
 a subset of the grid of 2^e, so it never has the smaller error and the rule reduces to max-to-6 (the
-OCP rule, rule "6"); the library implements max-to-6.  A block of zeros takes e = 0.  Codes pack two
-per byte, the even element in the low nibble.
+OCP rule, rule "6"); the library implements max-to-6.  A block of zeros takes e = 0; E8M0 holds
+2^-127 .. 2^127, so a block whose maximum is below 6 * 2^-127 takes e = -127.  Codes pack two per
+byte, the even element in the low nibble; the scale byte is e + 127.
 """
 from __future__ import annotations
 
@@ -81,9 +82,9 @@ def mx4_quantize_ref(x, rule: str = "6") -> tuple:
             amax = float(np.abs(blk).max())
             if amax == 0.0:
                 continue
-            e6 = smallest_exponent(amax, 6.0)
+            e6 = max(smallest_exponent(amax, 6.0), -127)
             best = None
-            for e in ([e6, smallest_exponent(amax, 4.0)] if rule == "4over6" else [e6]):
+            for e in ([e6, max(smallest_exponent(amax, 4.0), -127)] if rule == "4over6" else [e6]):
                 c = e2m1_encode(blk / 2.0 ** e)
                 err = math.fsum((dec[c] * 2.0 ** e - blk) ** 2)
                 if best is None or err < best[0]:

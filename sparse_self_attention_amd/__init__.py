@@ -13,6 +13,8 @@ missing or cannot be loaded, every call raises.
     out = delta_forward(q, k, v, idx, counts, 192, lse=lse, out_prev=out, fresh=fresh)  # sparse delta
     codes, vscale, vmean = vsmooth_quantize(v)             # V-Smooth E4M3 codes, scales, block means
     out, lse    = fp8_forward(q, k, codes, vscale, vmean, idx, counts, group=128)   # ExpCast + FP8 P.V
+    q4, qs = mx4_quantize(q); k4, ks = mx4_quantize(k)   # MXFP4 queries and keys
+    out, lse    = fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, idx, counts, group=128)  # 4-bit QK^T
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ from typing import Optional
 import torch
 
 __all__ = ["mask", "forward", "attn", "cached_mask", "colsum_mask", "delta_forward", "vsmooth_quantize",
-           "fp8_forward", "vsmooth_workspace_bytes", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
+           "fp8_forward", "mx4_quantize", "fp4_forward", "vsmooth_workspace_bytes", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
            "library_path", "SattnError", "TOPK", "THRESH"]
 
 TOPK, THRESH = 0, 1
@@ -77,6 +79,10 @@ def _load():
     lib.sattn_vsmooth_quantize.restype = I
     lib.sattn_fp8_forward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, P]
     lib.sattn_fp8_forward.restype = I
+    lib.sattn_mx4_quantize.argtypes = [P, I, I, I, I, P, P, P]
+    lib.sattn_mx4_quantize.restype = I
+    lib.sattn_fp4_forward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, P]
+    lib.sattn_fp4_forward.restype = I
     lib.sattn_voxel_permutation.argtypes = [I, I, I, I, I, I, P]
     lib.sattn_voxel_permutation.restype = I
     lib.sattn_permute_tokens.argtypes = [P, P, P, I, I, I, I, I, P]
@@ -334,6 +340,62 @@ def fp8_forward(q: torch.Tensor, k: torch.Tensor, codes: torch.Tensor, vscale: t
                                idx.shape[-1], B, H, Nq, Nk, D, group, scale, _ptr(out),
                                F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
     _check("sattn_fp8_forward", st)
+    return out, lse
+
+
+def mx4_quantize(x: torch.Tensor, *, codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """MXFP4 quantisation of bf16 queries or keys (sattn_mx4_quantize): returns (codes uint8 [B,H,N,D/2],
+    scales uint8 [B,H,N,4])."""
+    lib = _load()
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [B, H, N, D] device tensor")
+    B, H, N, D = x.shape
+    if codes is None:
+        codes = torch.empty((B, H, N, D // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, N, 4), dtype=torch.uint8, device=x.device)
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, N, D // 2) or scales.dtype != torch.uint8
+            or tuple(scales.shape) != (B, H, N, 4) or not codes.is_contiguous() or not scales.is_contiguous()):
+        raise ValueError("codes must be contiguous uint8 [B,H,N,D/2] and scales uint8 [B,H,N,4]")
+    _check("sattn_mx4_quantize", lib.sattn_mx4_quantize(_ptr(x), B, H, N, D, _ptr(codes), _ptr(scales), _stream_ptr(x)))
+    return codes, scales
+
+
+def fp4_forward(q4: torch.Tensor, q_scales: torch.Tensor, k4: torch.Tensor, k_scales: torch.Tensor,
+                codes: torch.Tensor, vscale: torch.Tensor, vmean: torch.Tensor, idx: torch.Tensor,
+                counts: torch.Tensor, group: int, *, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32, want_lse: bool = True):
+    """4-bit QK^T + FP8 value path (sattn_fp4_forward).  Returns (out, lse)."""
+    lib = _load()
+    for name, t in (("q4", q4), ("k4", k4), ("q_scales", q_scales), ("k_scales", k_scales)):
+        if not t.is_cuda or t.dtype != torch.uint8 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 [B, H, N, *] device tensor")
+    B, H, Nq, D2 = q4.shape
+    D = 2 * D2
+    Nk = k4.shape[2]
+    if tuple(k4.shape) != (B, H, Nk, D2) or tuple(q_scales.shape) != (B, H, Nq, 4) or tuple(k_scales.shape) != (B, H, Nk, 4):
+        raise ValueError("q4 / k4 must be [B,H,N,D/2] and their scales [B,H,N,4] (mx4_quantize)")
+    G = -(-Nq // group)
+    S = lib.sattn_vsmooth_mean_stride(Nk)
+    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
+        raise ValueError("idx and counts must be contiguous int32")
+    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
+        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, Nk, D) or vscale.dtype != torch.float32
+            or tuple(vscale.shape) != (B, H, D) or vmean.dtype != torch.bfloat16 or tuple(vmean.shape) != (B, H, D, S)
+            or not (codes.is_contiguous() and vscale.is_contiguous() and vmean.is_contiguous())):
+        raise ValueError("codes, vscale, vmean must be what vsmooth_quantize returns for V")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q4.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (B, H, Nq, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or fp32 [B, H, Nq, D] tensor")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q4.device)
+    st = lib.sattn_fp4_forward(_ptr(q4), _ptr(q_scales), _ptr(k4), _ptr(k_scales), _ptr(codes), _ptr(vscale), _ptr(vmean),
+                               _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk, D, group, scale, _ptr(out),
+                               F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q4))
+    _check("sattn_fp4_forward", st)
     return out, lse
 
 

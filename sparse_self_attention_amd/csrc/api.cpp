@@ -272,8 +272,51 @@ int sattn_fp8_forward(const void* q, const void* k, const uint8_t* codes, const 
     if (err) return hip_fail(err, fn);
     if (flag) return fail(SATTN_ERR_INDEX, "%s: index lists invalid (code %d)", fn, flag);
   }
-  sattn::Fp8FwdArgs a{q, k, codes, vscale, vmean, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out,
+  sattn::Fp8FwdArgs a{q, k, nullptr, nullptr, codes, vscale, vmean, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out,
                       out_dtype == SATTN_F32, lse, stream};
+  const int err = sattn::launch_fp8_fwd(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
+int sattn_mx4_quantize(const void* x, int B, int H, int N, int D, uint8_t* codes, uint8_t* scales, void* stream) {
+  static const char* fn = "sattn_mx4_quantize";
+  if (!x || !codes || !scales) return fail(SATTN_ERR_NULL, "%s: x, codes and scales must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, N, 1, D)) return r;
+  if ((int64_t)B * H * N * (D / 32) >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many blocks", fn);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(SATTN_ERR_ARG, "%s: x and codes must be 16-byte aligned, scales 4-byte aligned", fn);
+  sattn::Mx4QuantArgs a{x, B, H, N, D, codes, scales, stream};
+  const int err = sattn::launch_mx4_quant(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
+int sattn_fp4_forward(const uint8_t* q4, const uint8_t* q_scales, const uint8_t* k4, const uint8_t* k_scales,
+                      const uint8_t* codes, const float* vscale, const void* vmean, const int32_t* idx,
+                      const int32_t* counts, int cap, int B, int H, int Nq, int Nk, int D, int group, float scale,
+                      void* out, int out_dtype, float* lse, void* stream) {
+  static const char* fn = "sattn_fp4_forward";
+  if (!q4 || !q_scales || !k4 || !k_scales || !codes || !vscale || !vmean || !idx || !counts || !out)
+    return fail(SATTN_ERR_NULL, "%s: every input and out must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
+  if (int r = check_group(fn, group)) return r;
+  if (int r = check_scale(fn, scale)) return r;
+  if (cap < 1) return fail(SATTN_ERR_ARG, "%s: cap = %d must be >= 1", fn, cap);
+  if (out_dtype != SATTN_BF16 && out_dtype != SATTN_F32) return fail(SATTN_ERR_ARG, "%s: bad out_dtype", fn);
+  if (!aligned(q4, 16) || !aligned(k4, 16) || !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(codes, 16) ||
+      !aligned(vscale, 16) || !aligned(vmean, 16) || !aligned(out, 16) || !aligned(idx, 4) || !aligned(counts, 4) ||
+      !aligned(lse, 4))
+    return fail(SATTN_ERR_ARG, "%s: q4, k4, codes, vscale, vmean, out 16-byte; scales, idx, counts, lse 4-byte aligned",
+                fn);
+  const int64_t G = (Nq + group - 1) / group;
+  if ((int64_t)B * H * G >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many groups", fn);
+  if (validate_mode()) {
+    int flag = 0;
+    const int err = sattn::validate_index_lists(idx, counts, cap, (int)(B * H * G), Nk, stream, &flag);
+    if (err) return hip_fail(err, fn);
+    if (flag) return fail(SATTN_ERR_INDEX, "%s: index lists invalid (code %d)", fn, flag);
+  }
+  sattn::Fp8FwdArgs a{q4, k4, q_scales, k_scales, codes, vscale, vmean, idx, counts, cap, B, H, Nq, Nk, D, group,
+                      scale, out, out_dtype == SATTN_F32, lse, stream};
   const int err = sattn::launch_fp8_fwd(a);
   return err ? hip_fail(err, fn) : SATTN_OK;
 }

@@ -199,28 +199,95 @@ int launch_vsmooth(const VsmoothArgs& a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// MXFP4 quantisation of queries and keys (4-bit QK^T)
+// ---------------------------------------------------------------------------------------------
+
+// Nearest E2M1 code of y (|y| <= 6), ties to the even code: the magnitude index counts the midpoints
+// passed, strictly where the lower neighbour is even and inclusively where the upper one is.
+__device__ inline uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return y < 0.0f ? (c | 8u) : c;
+}
+
+// One thread per (row, block of 32): scale 2^e with the smallest e such that 6 * 2^e >= max |x|
+// (at least 2^-127; 2^0 for a zero block), codes of x / 2^e packed two per byte (even element low).
+// Scales take 4 bytes a row (byte b = block b; at D = 64 bytes 2 and 3 hold 127, i.e. 1.0).
+template <int D>
+__global__ __launch_bounds__(256) void k_mx4_quant(const uint16_t* __restrict__ x, uint32_t nrows,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int NB = D / 32;
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= nrows * (uint32_t)NB) return;
+  const uint32_t row = t / NB, b = t % NB;
+  const u32x4* src = (const u32x4*)(x + (size_t)row * D + b * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 w = src[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[8 * i + j] = bf16_bits_to_float((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = 0;
+  if (amax > 0.0f) {
+    int xe;
+    const float f = frexpf(amax, &xe);    // amax = f 2^xe, 0.5 <= f < 1; 6 = 0.75 * 2^3
+    e = max(f <= 0.75f ? xe - 3 : xe - 2, -127);
+  }
+  const float inv = ldexpf(1.0f, -e);     // exact: x / 2^e for bf16 x
+  u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) out[i >> 3] |= e2m1_code(v[i] * inv) << (4 * (i & 7));
+  *(u32x4*)(codes + (size_t)row * (D / 2) + b * 16) = out;
+  scales[(size_t)row * 4 + b] = (uint8_t)(e + 127);
+  if (NB == 2) scales[(size_t)row * 4 + 2 + b] = 127;
+}
+
+int launch_mx4_quant(const Mx4QuantArgs& a) {
+  const uint32_t nrows = (uint32_t)a.B * (uint32_t)a.H * (uint32_t)a.N;
+  const uint32_t threads = nrows * (uint32_t)(a.D / 32);
+  const dim3 grid((threads + 255) / 256);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_mx4_quant<128>, grid, dim3(256), 0, st, (const uint16_t*)a.x, nrows, a.codes, a.scales);
+  else
+    hipLaunchKernelGGL(k_mx4_quant<64>, grid, dim3(256), 0, st, (const uint16_t*)a.x, nrows, a.codes, a.scales);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 // Sparse forward with ExpCast bytes and the FP8 P.V product
 // ---------------------------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool QK4 = false>
 struct F8Layout {
-  static constexpr int RB = 2 * D;                 // bytes per bf16 K row
-  static constexpr int NC = D / 8;                 // 16-byte chunks per K row
+  // K rows in LDS: bf16 (2D bytes), or E2M1 codes (D/2 bytes) followed by a region of per-key E8M0
+  // scales (D/32 bytes per key) for the 4-bit product
+  static constexpr int RB = QK4 ? D / 2 : 2 * D;
+  static constexpr int NC = RB / 16;               // 16-byte chunks per K row
   static constexpr int RPL = 1024 / RB;            // K rows filled by one 64-lane 16-byte load
   static constexpr int KSETS = F8_BK / RPL;        // K loads per tile
+  static constexpr int KSB = 4;                    // scale bytes per row (4-bit product; D / 32 used)
   static constexpr int NC8 = D / 16;               // 16-byte chunks per E4M3 V row
   static constexpr int RPL8 = 1024 / D;            // V rows per load
   static constexpr int VSETS = F8_BK / RPL8;       // V loads per tile
-  static constexpr int KBYTES = F8_BK * RB;
+  static constexpr int KBYTES = F8_BK * RB + (QK4 ? 1024 : 0);   // codes + scale region (1 KB aligned)
+  static constexpr int KSOFF = F8_BK * RB;                      // offset of the scale region
   static constexpr int VBYTES = F8_BK * D;
   static constexpr int IBYTES = F8_BK * 32;        // one 32-byte slot row per key
   static constexpr int STAGE = KBYTES + VBYTES + IBYTES;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
-  static constexpr int ROWDIV = 16 / NC;
+  static constexpr int ROWDIV = QK4 ? 4 : 16 / NC;
   // register budget: two waves per SIMD at D = 128 (O, both score halves, Q and the slot sums
   // stay in VGPRs), three at D = 64
   static constexpr int WAVES_PER_EU = D == 128 ? 2 : 3;
+  // bf16 K: 16 rows read at one chunk hit distinct banks; E2M1 K (64- or 32-byte rows read 16 bytes a
+  // lane): rows r and r + 4 of a 64-byte-row tile trade chunks
   __device__ static inline int swz_k(int row) { return (row / ROWDIV) % NC; }
   // 32-byte pair of a V row: the transposing read takes rows {0,1,2,3,8,9,10,11} (+4h, +16t) at one
   // pair index; this XOR spreads them over all 64 banks
@@ -267,14 +334,17 @@ __device__ inline uint32_t key_byte_mask(uint64_t m64, int w, int h) {
   return (spread << 8) - spread;
 }
 
-template <int D, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layout<D>::WAVES_PER_EU,
-                                                                         F8Layout<D>::WAVES_PER_EU))) void attn_fwd_fp8(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint8_t* __restrict__ v8,
+// QK4: Q and K arrive as E2M1 codes (D/2 bytes a row) with E8M0 scales per 32 elements (qs, ks) and the
+// scores come from v_mfma_scale_f32_32x32x64_f8f6f4 in FP4 x FP4, two products per 32-key half at D = 128.
+template <int D, int NW, bool OUT_F32, bool QK4>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layout<D, QK4>::WAVES_PER_EU,
+                                                                         F8Layout<D, QK4>::WAVES_PER_EU))) void attn_fwd_fp8(
+    const void* __restrict__ qv, const void* __restrict__ kv, const uint8_t* __restrict__ qs,
+    const uint8_t* __restrict__ ks, const uint8_t* __restrict__ v8,
     const float* __restrict__ vscale, const uint16_t* __restrict__ vmean, int nbp,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap, int Nq, int Nk, int group, int G,
     float scale_log2, void* __restrict__ out, float* __restrict__ lse, uint32_t n_units) {
-  using L = F8Layout<D>;
+  using L = F8Layout<D, QK4>;
   constexpr int NKS = (L::KSETS + NW - 1) / NW;
   constexpr int NVS = (L::VSETS + NW - 1) / NW;
   constexpr int ISETS = L::IBYTES / 1024;          // slot-row loads per tile (2)
@@ -296,19 +366,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   int c = counts[bh * (uint32_t)G + g];
   c = c < 0 ? 0 : (c > cap ? cap : c);
   const int nblk = (c + F8_BK - 1) / F8_BK;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)kv + (size_t)bh * Nk * L::RB, (uint32_t)Nk * L::RB);
+  const __amdgpu_buffer_rsrc_t rks =
+      make_rsrc(QK4 ? ks + (size_t)bh * Nk * L::KSB : nullptr, QK4 ? (uint32_t)Nk * L::KSB : 0u);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8 + (size_t)bh * Nk * D, (uint32_t)Nk * D);
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(vmean + (size_t)bh * D * nbp, (uint32_t)(D * nbp * 2));
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(k_onehot.b, (uint32_t)sizeof(k_onehot.b));
   const int32_t* ilist = idx + ((size_t)bh * G + g) * (size_t)cap;
 
-  bf16x8 qf[L::KSTEPS];
+  // the wave's query rows: bf16 (8 k-steps of 16 dims) or E2M1 (D/64 steps of 64 dims, 16 bytes a lane)
+  constexpr int QREGS = QK4 ? D / 64 : L::KSTEPS;
+  u32x4 qf[QREGS];
+  uint32_t qscale = 0;     // E8M0 scales of the lane's blocks 2t + hi, in byte 2t after the shift
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (size_t)bh * Nq * D, (uint32_t)Nq * L::RB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)qv + (size_t)bh * Nq * L::RB, (uint32_t)Nq * L::RB);
     const uint32_t rowoff = row_valid ? (uint32_t)(r0 + wrow) * L::RB : (uint32_t)Nq * L::RB;
 #pragma unroll
-    for (int ks = 0; ks < L::KSTEPS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, buffer_load_x4(rq, rowoff + (uint32_t)(2 * ks + hi) * 16));
+    for (int t = 0; t < QREGS; ++t) qf[t] = buffer_load_x4(rq, rowoff + (uint32_t)(2 * t + hi) * 16);
+    if constexpr (QK4) {
+      const uint8_t* qsr = qs + ((size_t)bh * Nq + r0 + (row_valid ? wrow : 0)) * L::KSB;
+      qscale = *(const uint32_t*)qsr >> (8 * hi);
+    }
   }
   // per-lane offsets are recomputed where used (a few integer operations) rather than held in VGPRs
   const uint32_t kbase = ql * L::RB;
@@ -337,7 +415,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   // slot-row load of this wave (waves 0 and 1): LDS position 32 wave + lane / 2 holds key row
   // ind_pos(position), chunk lane % 2
   const int irow = ind_pos(32 * wave + (lane >> 1));
-  int kkeys[NKS], vkeys[NVS], ikey = 0;
+  int kkeys[NKS], vkeys[NVS], ikey = 0, skey = 0;
+  const int swave = NW - 1;        // the wave that gathers the keys' E8M0 scales (4-bit product)
   auto fetch_keys = [&](int blk) {
 #pragma unroll
     for (int j = 0; j < NKS; ++j) {
@@ -354,6 +433,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     if (wave < ISETS) {
       const int p = blk * F8_BK + irow;
       ikey = ilist[p < c ? p : c - 1];
+    }
+    if (QK4 && wave == swave) {
+      const int p = blk * F8_BK + lane;
+      skey = ilist[p < c ? p : c - 1];
     }
   };
   auto issue = [&](char* stage) {
@@ -372,6 +455,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     if (wave < ISETS)
       buffer_load_lds_x4(ro, stage + L::KBYTES + L::VBYTES + wave * 1024,
                          (uint32_t)((ikey >> 7) & (F8_WIN - 1)) * 32u + 16u * (uint32_t)(lane & 1));
+    if (QK4 && wave == swave)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, SATTN_LDS_PTR(void, stage + L::KSOFF), L::KSB,
+                                               (uint32_t)skey * L::KSB, 0, 0, 0);
   };
   // the tile's listed key of this lane (lane = position in the tile), for the mean windows
   auto tile_key = [&](int blk) {
@@ -429,12 +515,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     const char* sk = smem + ST * L::STAGE;
     const char* sv = sk + L::KBYTES;
     f32x16 s0 = {}, s1 = {};
+    if constexpr (QK4) {
+      // E8M0 scales of keys ql and 32 + ql, shifted so byte 2t holds block 2t + hi
+      const char* sks = sk + L::KSOFF;
+      const uint32_t k0s = *(const uint32_t*)(sks + ql * 4) >> (8 * hi);
+      const uint32_t k1s = *(const uint32_t*)(sks + (32 + ql) * 4) >> (8 * hi);
+      // one k-step of 64 dims; the scale byte select (2t) must be an immediate
+      auto kstep = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        const u32x4 a0 = *(const u32x4*)(sk + koff(t));
+        const u32x4 a1 = *(const u32x4*)(sk + 32 * L::RB + koff(t));
+        const i32x8 b8 = {(int)qf[t][0], (int)qf[t][1], (int)qf[t][2], (int)qf[t][3], 0, 0, 0, 0};
+        const i32x8 a08 = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], 0, 0, 0, 0};
+        const i32x8 a18 = {(int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3], 0, 0, 0, 0};
+        s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a08, b8, s0, 4, 4, 2 * t, (int)k0s, 2 * t, (int)qscale);
+        s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a18, b8, s1, 4, 4, 2 * t, (int)k1s, 2 * t, (int)qscale);
+      };
+      kstep(F8IC<0>{});
+      if constexpr (QREGS > 1) kstep(F8IC<1>{});
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < L::KSTEPS; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(sk + koff(ks));
-      const bf16x8 a1 = *(const bf16x8*)(sk + 32 * L::RB + koff(ks));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+      for (int ks = 0; ks < L::KSTEPS; ++ks) {
+        const bf16x8 a0 = *(const bf16x8*)(sk + koff(ks));
+        const bf16x8 a1 = *(const bf16x8*)(sk + 32 * L::RB + koff(ks));
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8, qf[ks]), s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8, qf[ks]), s1, 0, 0, 0);
+      }
     }
     const int valid = min(F8_BK, c - j * F8_BK);
     if (valid < F8_BK) {
@@ -561,7 +667,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool QK4>
 static int launch_fp8_t(const Fp8FwdArgs& a) {
   const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
   const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
@@ -569,25 +675,29 @@ static int launch_fp8_t(const Fp8FwdArgs& a) {
   const int nbp = vsmooth_mean_stride(a.Nk);
   hipStream_t st = (hipStream_t)a.stream;
   if (a.out_f32)
-    hipLaunchKernelGGL((attn_fwd_fp8<D, NW, true>), dim3(n_units), dim3(NW * 64), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap,
-                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+    hipLaunchKernelGGL((attn_fwd_fp8<D, NW, true, QK4>), dim3(n_units), dim3(NW * 64), 0, st, a.q, a.k, a.q_scales,
+                       a.k_scales, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap, a.Nq,
+                       a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
   else
-    hipLaunchKernelGGL((attn_fwd_fp8<D, NW, false>), dim3(n_units), dim3(NW * 64), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap,
-                       a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+    hipLaunchKernelGGL((attn_fwd_fp8<D, NW, false, QK4>), dim3(n_units), dim3(NW * 64), 0, st, a.q, a.k, a.q_scales,
+                       a.k_scales, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap, a.Nq,
+                       a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
   return (int)hipGetLastError();
 }
 
-template <int D>
+template <int D, bool QK4>
 static int launch_fp8_d(const Fp8FwdArgs& a) {
   const int waves = (a.group + 31) / 32;
-  if (waves <= 2) return launch_fp8_t<D, 2>(a);
-  if (waves <= 4) return launch_fp8_t<D, 4>(a);
-  if (waves <= 6) return launch_fp8_t<D, 6>(a);
-  return launch_fp8_t<D, 8>(a);
+  if (waves <= 2) return launch_fp8_t<D, 2, QK4>(a);
+  if (waves <= 4) return launch_fp8_t<D, 4, QK4>(a);
+  if (waves <= 6) return launch_fp8_t<D, 6, QK4>(a);
+  return launch_fp8_t<D, 8, QK4>(a);
 }
 
-int launch_fp8_fwd(const Fp8FwdArgs& a) { return a.D == 64 ? launch_fp8_d<64>(a) : launch_fp8_d<128>(a); }
+int launch_fp8_fwd(const Fp8FwdArgs& a) {
+  const bool qk4 = a.q_scales != nullptr;
+  if (a.D == 64) return qk4 ? launch_fp8_d<64, true>(a) : launch_fp8_d<64, false>(a);
+  return qk4 ? launch_fp8_d<128, true>(a) : launch_fp8_d<128, false>(a);
+}
 
 }  // namespace sattn

@@ -108,8 +108,10 @@ struct VsmoothArgs {
 int launch_vsmooth(const VsmoothArgs& a);
 
 struct Fp8FwdArgs {
-  const void* q;
-  const void* k;
+  const void* q;                  // bf16 Q, or E2M1 codes of Q when q_scales is set
+  const void* k;                  // bf16 K, or E2M1 codes of K when k_scales is set
+  const uint8_t* q_scales;        // E8M0 block scales of Q and K (4-bit QK^T), else nullptr
+  const uint8_t* k_scales;
   const uint8_t* codes;
   const float* vscale;
   const void* vmean;
@@ -124,6 +126,17 @@ struct Fp8FwdArgs {
   void* stream;
 };
 int launch_fp8_fwd(const Fp8FwdArgs& a);
+
+// MXFP4 codes [B,H,N,D/2] (two per byte, even element low) and E8M0 scales [B,H,N,4] (block b at byte b,
+// D/32 blocks used) of bf16 rows.
+struct Mx4QuantArgs {
+  const void* x;
+  int B, H, N, D;
+  uint8_t* codes;
+  uint8_t* scales;
+  void* stream;
+};
+int launch_mx4_quant(const Mx4QuantArgs& a);
 
 int launch_permute_tokens(const void* src, void* dst, const int32_t* perm, int BH, int N, int D, int inverse,
                           void* stream);

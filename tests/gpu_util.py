@@ -81,3 +81,46 @@ def workload(name: str):
 
 def scale_of(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+def _stride(nk):
+    return 4 * (-(-(-(-nk // 128)) // 4))
+
+
+def vsmooth_to_device(codes, scale, mean, nk, dev="cuda:0"):
+    """The oracle's (codes, scale, mean [B,H,NB,D]) in the library's layout: mean / scale channel-major,
+    padded with zeros to the stride (exact: the scale is a power of two)."""
+    import torch
+    B, H, NB, D = mean.shape
+    m = np.zeros((B, H, D, _stride(nk)), dtype=np.float32)
+    m[:, :, :, :NB] = np.transpose(mean / scale[:, :, None, :], (0, 1, 3, 2))
+    mb = inputs.f32_to_bf16_bits(m)
+    assert np.array_equal(inputs.bf16_bits_to_f32(mb), m), "scaled means must be exact in bf16"
+    return (torch.from_numpy(np.ascontiguousarray(codes)).to(dev), torch.from_numpy(scale.astype(np.float32)).to(dev),
+            to_device_bf16(mb, dev))
+
+
+def structured_lists(rng, B, H, G, Nk, counts, kind):
+    cap = max(1, int(counts.max()))
+    if kind == "random":
+        return inputs.random_index_lists(rng, B, H, G, Nk, counts, cap)
+    idx = np.full((B, H, G, cap), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                c = int(counts[b, h, g])
+                if kind == "spread":           # one key per 128-token block: 64 blocks in every tile
+                    base = rng.integers(0, 128, size=c)
+                    keys = np.minimum(np.arange(c) * 128 + base, Nk - 1)
+                    keys = np.unique(keys)
+                    counts[b, h, g] = keys.size
+                elif kind == "jumps":          # runs of 20 keys with gaps of ~40 blocks between runs
+                    starts = np.cumsum(rng.integers(4000, 6000, size=-(-c // 20)))
+                    keys = np.unique(np.minimum((starts[:, None] + np.arange(20)[None]).ravel()[:c], Nk - 1))
+                    counts[b, h, g] = keys.size
+                else:                          # one block
+                    keys = np.sort(rng.choice(128, size=min(c, 128), replace=False)) + 128 * (g % max(1, Nk // 128))
+                    keys = keys[keys < Nk]
+                    counts[b, h, g] = keys.size
+                idx[b, h, g, :keys.size] = keys
+    return idx

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"sattn_mask", "sattn_forward", "attn_forward", "sattn_mask_workspace_bytes", "sattn_cached_mask",
             "sattn_colsum_mask", "sattn_delta_forward", "sattn_vsmooth_quantize", "sattn_fp8_forward",
-            "sattn_vsmooth_workspace_bytes", "sattn_vsmooth_mean_stride",
+            "sattn_vsmooth_workspace_bytes", "sattn_vsmooth_mean_stride", "sattn_mx4_quantize", "sattn_fp4_forward",
             "sattn_strerror", "sattn_last_error", "sattn_voxel_permutation", "sattn_permute_tokens"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sattn.h but not exported"
@@ -190,6 +190,37 @@ FP8_CASES = [
 @pytest.mark.parametrize("kw,code", FP8_CASES, ids=[str(c[0]) for c in FP8_CASES])
 def test_fp8_forward_validation(lib, kw, code):
     assert f8f(lib, **kw) == code
+    assert lib.sattn_last_error()
+
+
+def mxq(lib, x=FAKE, B=1, H=1, N=64, D=128, codes=FAKE, scales=FAKE):
+    return lib.sattn_mx4_quantize(x, B, H, N, D, codes, scales, P(0))
+
+
+MX4_CASES = [(dict(x=P(0)), ERR_NULL), (dict(scales=P(0)), ERR_NULL), (dict(N=0), ERR_SHAPE), (dict(D=96), ERR_UNSUPPORTED),
+             (dict(codes=P(4104)), ERR_ARG), (dict(scales=P(4098)), ERR_ARG), (dict(x=P(4100)), ERR_ARG)]
+
+
+@pytest.mark.parametrize("kw,code", MX4_CASES, ids=[str(c[0]) for c in MX4_CASES])
+def test_mx4_quantize_validation(lib, kw, code):
+    assert mxq(lib, **kw) == code
+    assert lib.sattn_last_error()
+
+
+def f4f(lib, q4=FAKE, qs=FAKE, k4=FAKE, ks=FAKE, codes=FAKE, vscale=FAKE, vmean=FAKE, idx=FAKE, counts=FAKE, cap=64,
+        B=1, H=1, Nq=128, Nk=128, D=128, group=128, scale=0.1, out=FAKE, out_dtype=1, lse=P(0)):
+    return lib.sattn_fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, idx, counts, cap, B, H, Nq, Nk, D, group, scale,
+                                 out, out_dtype, lse, P(0))
+
+
+FP4_CASES = [(dict(q4=P(0)), ERR_NULL), (dict(ks=P(0)), ERR_NULL), (dict(vmean=P(0)), ERR_NULL), (dict(Nk=0), ERR_SHAPE),
+             (dict(D=32), ERR_UNSUPPORTED), (dict(group=20), ERR_UNSUPPORTED), (dict(scale=float("inf")), ERR_ARG),
+             (dict(cap=0), ERR_ARG), (dict(out_dtype=4), ERR_ARG), (dict(k4=P(4104)), ERR_ARG), (dict(qs=P(4098)), ERR_ARG)]
+
+
+@pytest.mark.parametrize("kw,code", FP4_CASES, ids=[str(c[0]) for c in FP4_CASES])
+def test_fp4_forward_validation(lib, kw, code):
+    assert f4f(lib, **kw) == code
     assert lib.sattn_last_error()
 
 

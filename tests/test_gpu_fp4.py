@@ -1,0 +1,139 @@
+"""GPU parity of the 4-bit QK^T path: MXFP4 quantisation of queries and keys (sattn_mx4_quantize, bit-exact
+against the oracle) and the FP4-score / FP8-value forward (sattn_fp4_forward) against the fp64 oracle fed
+the oracle's own codes and scales."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_lse, check_out, f64, scale_of, structured_lists, to_device_bf16, vsmooth_to_device, workload
+from synth import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def sattn():
+    import sparse_self_attention_amd as s
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert os.path.exists(s.library_path()), "libsattn.so is not built"
+    return s
+
+
+def _pack(codes, exps):
+    """The oracle's unpacked codes and exponents in the library's layout: two codes a byte (even element in the
+    low nibble), four scale bytes a row (e + 127; unused bytes 127)."""
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    sc = np.full(exps.shape[:-1] + (4,), 127, dtype=np.uint8)
+    sc[..., :exps.shape[-1]] = (exps + 127).astype(np.uint8)
+    return packed, sc
+
+
+def _check_quant(sattn, xb, what):
+    x = to_device_bf16(xb, DEV)
+    codes, scales = sattn.mx4_quantize(x)
+    torch.cuda.synchronize()
+    rc, re = oracle.mx4_quantize_ref(f64(xb))
+    pc, ps = _pack(rc, re)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    bad = np.argwhere(gc != pc)
+    assert bad.size == 0, f"{what}: {len(bad)} code bytes differ, first at {bad[0]}"
+    assert np.array_equal(gs, ps), f"{what}: scale bytes differ"
+    return rc, re
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_mx4_quantize_bit_exact(sattn, D):
+    rng = np.random.default_rng(D)
+    x = rng.standard_normal((2, 3, 157, D)) * np.exp(rng.uniform(-6, 6, size=(2, 3, 157, 1)))
+    x[0, 0, 0] = 0.0                                     # zero blocks
+    x[0, 1, 1, :32] = np.linspace(-5.99, 6.0, 32)        # ties and the top code
+    x[1, 2, 3, :] = 1e-38                                # a block below 6 * 2^-127
+    xb = inputs.f32_to_bf16_bits(x.astype(np.float32))
+    _check_quant(sattn, xb, f"D={D}")
+
+
+def _run(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0):
+    B, H = 1, 2
+    G = -(-Nq // group)
+    qb = inputs.f32_to_bf16_bits((rng.standard_normal((B, H, Nq, D)) * q_std).astype(np.float32))
+    kb = inputs.f32_to_bf16_bits(rng.standard_normal((B, H, Nk, D)).astype(np.float32))
+    off = np.repeat(rng.uniform(-2, 2, size=(H, -(-Nk // 128), 1)), 128, axis=1)[:, :Nk][None]
+    vb = inputs.f32_to_bf16_bits((rng.standard_normal((B, H, Nk, D)) + off).astype(np.float32))
+    counts = rng.integers(1, cmax + 1, size=(B, H, G)).astype(np.int32)
+    counts[0, 0, 0] = cmax
+    if G > 1:
+        counts[0, 1, G - 1] = 0
+    idx = structured_lists(rng, B, H, G, Nk, counts, kind)
+    qc, qe = oracle.mx4_quantize_ref(f64(qb))
+    kc, ke = oracle.mx4_quantize_ref(f64(kb))
+    vc, vs, vm = oracle.vsmooth_quantize_ref(f64(vb))
+    scale = scale_of(D)
+    ro, rl = oracle.fp4_attention_ref(qc, qe, kc, ke, vc, vs, vm, idx, counts, group, scale)
+    q4, qs = (torch.from_numpy(a).to(DEV) for a in _pack(qc, qe))
+    k4, ks = (torch.from_numpy(a).to(DEV) for a in _pack(kc, ke))
+    codes, vscale, vmean = vsmooth_to_device(vc, vs, vm, Nk)
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    out, lse = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
+    check_out(out.cpu().numpy(), ro, what)
+    check_lse(lse.cpu().numpy(), rl, what)
+
+
+FWD_CASES = [
+    (128, 128, 300, 3000, 700, "random"),
+    (64, 64, 200, 5000, 1500, "random"),
+    (128, 192, 400, 9000, 70, "spread"),
+    (64, 256, 300, 70000, 200, "jumps"),
+    (128, 16, 50, 1000, 128, "one"),
+]
+
+
+@pytest.mark.parametrize("D,group,Nq,Nk,cmax,kind", FWD_CASES)
+def test_fp4_forward(sattn, D, group, Nq, Nk, cmax, kind):
+    rng = np.random.default_rng(D * 11 + group + Nq + Nk)
+    _run(sattn, rng, D, group, Nq, Nk, cmax, kind)
+
+
+def test_fp4_forward_large_logits(sattn):
+    _run(sattn, np.random.default_rng(9), 128, 128, 256, 4000, 900, "random", q_std=6.0)
+
+
+def test_fp4_full_size_sampled(sattn):
+    """The long-video workload in the benchmark's launch configuration: MXFP4 of head 0's queries and keys
+    bit-exact; the forward over all 24 heads with head 0 on the oracle's quantisation, sampled groups."""
+    w, (qb, kb, vb) = workload("long_70200")
+    rng = np.random.default_rng(4)
+    qc, qe = _check_quant(sattn, qb[:, :1], "long_70200 q head 0")
+    kc, ke = _check_quant(sattn, kb[:, :1], "long_70200 k head 0")
+    vc, vs, vm = oracle.vsmooth_quantize_ref(f64(vb[:, :1]))
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    q4, qs = sattn.mx4_quantize(q)
+    k4, ks = sattn.mx4_quantize(k)
+    codes, vscale, vmean = sattn.vsmooth_quantize(v)
+    c0, s0, m0 = vsmooth_to_device(vc, vs, vm, w.n_k)
+    codes[:, :1].copy_(c0)
+    vscale[:, :1].copy_(s0)
+    vmean[:, :1].copy_(m0)
+    counts = np.full((1, w.heads, w.groups), w.topk, dtype=np.int32)
+    units = [0, w.groups // 3, w.groups - 1]
+    idx = np.zeros((1, w.heads, w.groups, w.topk), dtype=np.int32)
+    idx[:] = np.arange(w.topk, dtype=np.int32) * (w.n_k // w.topk)
+    for g in units:
+        idx[0, 0, g] = np.sort(rng.choice(w.n_k, size=w.topk, replace=False))
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    out, lse = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, ti, tc, w.group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    scale = scale_of(w.dim)
+    for g in units:
+        r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
+        ro, rl = oracle.fp4_attention_ref(qc[:, :, r], qe[:, :, r], kc, ke, vc, vs, vm, idx[:, :1, g:g + 1],
+                                          counts[:, :1, g:g + 1], w.group, scale)
+        check_out(out_h[:, :1, r], ro, f"long_70200 fp4 g={g}")
+        check_lse(lse_h[:, :1, r], rl, f"long_70200 fp4 g={g}")

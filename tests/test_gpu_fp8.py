@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import check_lse, check_out, f64, scale_of, to_device_bf16, workload
+from gpu_util import check_lse, check_out, f64, scale_of, to_device_bf16, workload, vsmooth_to_device, structured_lists
 from synth import inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,22 +30,6 @@ def _bits(rng, shape, std=1.0, offset=None):
     if offset is not None:
         x = x + offset
     return inputs.f32_to_bf16_bits(x.astype(np.float32))
-
-
-def _stride(nk):
-    return 4 * (-(-(-(-nk // 128)) // 4))
-
-
-def _to_device_quant(codes, scale, mean, nk):
-    """The oracle's (codes, scale, mean [B,H,NB,D]) in the library's layout: mean / scale channel-major,
-    padded with zeros to the stride (exact: the scale is a power of two)."""
-    B, H, NB, D = mean.shape
-    m = np.zeros((B, H, D, _stride(nk)), dtype=np.float32)
-    m[:, :, :, :NB] = np.transpose(mean / scale[:, :, None, :], (0, 1, 3, 2))
-    mb = inputs.f32_to_bf16_bits(m)
-    assert np.array_equal(inputs.bf16_bits_to_f32(mb), m), "scaled means must be exact in bf16"
-    return (torch.from_numpy(np.ascontiguousarray(codes)).to(DEV), torch.from_numpy(scale.astype(np.float32)).to(DEV),
-            to_device_bf16(mb, DEV))
 
 
 def _check_quant(sattn, vb, what):
@@ -82,32 +66,6 @@ def test_vsmooth_bit_exact(sattn, D, Nk, offsets):
     _check_quant(sattn, vb, f"D={D} Nk={Nk}")
 
 
-def _lists(rng, B, H, G, Nk, counts, kind):
-    cap = max(1, int(counts.max()))
-    if kind == "random":
-        return inputs.random_index_lists(rng, B, H, G, Nk, counts, cap)
-    idx = np.full((B, H, G, cap), -1, dtype=np.int32)
-    for b in range(B):
-        for h in range(H):
-            for g in range(G):
-                c = int(counts[b, h, g])
-                if kind == "spread":           # one key per 128-token block: 64 blocks in every tile
-                    base = rng.integers(0, 128, size=c)
-                    keys = np.minimum(np.arange(c) * 128 + base, Nk - 1)
-                    keys = np.unique(keys)
-                    counts[b, h, g] = keys.size
-                elif kind == "jumps":          # runs of 20 keys with gaps of ~40 blocks between runs
-                    starts = np.cumsum(rng.integers(4000, 6000, size=-(-c // 20)))
-                    keys = np.unique(np.minimum((starts[:, None] + np.arange(20)[None]).ravel()[:c], Nk - 1))
-                    counts[b, h, g] = keys.size
-                else:                          # one block
-                    keys = np.sort(rng.choice(128, size=min(c, 128), replace=False)) + 128 * (g % max(1, Nk // 128))
-                    keys = keys[keys < Nk]
-                    counts[b, h, g] = keys.size
-                idx[b, h, g, :keys.size] = keys
-    return idx
-
-
 def _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0, zero_group=True, out_bf16=False):
     B, H = 1, 2
     G = -(-Nq // group)
@@ -119,11 +77,11 @@ def _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0, zero_group=Tr
     counts[0, 0, 0] = cmax
     if zero_group and G > 1:
         counts[0, 1, G - 1] = 0
-    idx = _lists(rng, B, H, G, Nk, counts, kind)
+    idx = structured_lists(rng, B, H, G, Nk, counts, kind)
     rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
     scale = scale_of(D)
     ro, rl = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale)
-    codes, vscale, vmean = _to_device_quant(rc, rs, rm, Nk)
+    codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
     q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
     ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
     out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
@@ -172,7 +130,7 @@ def test_fp8_full_size_sampled(sattn):
     rc, rs, rm = _check_quant(sattn, vb[:, :1], "long_70200 head 0")
     q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
     codes, vscale, vmean = sattn.vsmooth_quantize(v)
-    c0, s0, m0 = _to_device_quant(rc, rs, rm, w.n_k)
+    c0, s0, m0 = vsmooth_to_device(rc, rs, rm, w.n_k)
     codes[:, :1].copy_(c0)
     vscale[:, :1].copy_(s0)
     vmean[:, :1].copy_(m0)

@@ -138,7 +138,7 @@ FP4_MUTANTS = [
     ("E2M1 level 3 read as 2.5", "_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)",
      "_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0)"),
     ("ties away from even", "((dhi == dlo) & (hi % 2 == 0))", "(dhi == dlo)"),
-    ("maximum scaled to 4", "e6 = smallest_exponent(amax, 6.0)", "e6 = smallest_exponent(amax, 4.0)"),
+    ("maximum scaled to 4", "e6 = max(smallest_exponent(amax, 6.0), -127)", "e6 = max(smallest_exponent(amax, 4.0), -127)"),
     ("scale one binade too small", "    e = math.ceil(math.log2(amax / top)) - 1\n    while top * 2.0 ** e < amax:",
      "    e = math.ceil(math.log2(amax / top)) - 2\n    while top * 2.0 ** e < amax / 2:"),
     ("blocks of 16", "MX_BLOCK = 32", "MX_BLOCK = 16"),
