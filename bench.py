@@ -314,7 +314,17 @@ def main():
                               "kept_tflops": round(kflops / (f8_ms * 1e-3) / 1e12, 2),
                               "speedup_vs_bf16_fwd": round(bf_ms / f8_ms, 3),
                               "rel_l2_vs_bf16_out": round(rel8, 5)}
-        del vws, codes, vscale, vmean, o8
+        # 4-bit QK^T on the same step and lists: MXFP4 queries and keys, FP8 value path
+        q4, q4s = sattn.mx4_quantize(q0)
+        k4, k4s = sattn.mx4_quantize(k0)
+        mx_ms = timed(lambda: (sattn.mx4_quantize(q0, codes=q4, scales=q4s), sattn.mx4_quantize(k0, codes=k4, scales=k4s)))
+        f4_ms = timed(lambda: sattn.fp4_forward(q4, q4s, k4, k4s, codes, vscale, vmean, idx, counts, w.group, out=o8,
+                                                lse=lse))
+        rel4 = ((o8.float() - out.float()).norm() / out.float().norm()).item()
+        rec["fp4_qk"] = {"mx4_quantize_qk_ms": round(mx_ms, 3), "fwd_ms": round(f4_ms, 3),
+                         "kept_tflops": round(kflops / (f4_ms * 1e-3) / 1e12, 2),
+                         "speedup_vs_bf16_fwd": round(bf_ms / f4_ms, 3), "rel_l2_vs_bf16_out": round(rel4, 5)}
+        del vws, codes, vscale, vmean, o8, q4, q4s, k4, k4s
     if not args.no_cpu_baseline and not args.kernel_only:
         # oracle on the step-0 inputs with the step-0 lists
         sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
