@@ -9,6 +9,8 @@
 // Mapping onto CDNA4
 // ------------------
 //  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32) of the group.
+//    Workgroup ids are striped over the XCDs in runs of 128 units, so the eight XCDs work on
+//    neighbouring groups of one head at a time (its K/V stay in the last-level cache).
 //  * Key blocks of 32 kept keys.  The block's K and V rows are gathered from HBM straight
 //    into LDS with 16-byte buffer-load-to-LDS instructions (one lane = one 16 B chunk of a row),
 //    double-buffered so the gather of block j+1 overlaps the math of block j.  Buffer loads
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_BYTES];
 
-  const uint32_t unit = xcd_contiguous(blockIdx.x, n_units);
+  const uint32_t unit = xcd_striped(blockIdx.x, n_units, 128);
   const int g = (int)(unit % (uint32_t)G);
   const uint32_t bh = unit / (uint32_t)G;
   const int lane = threadIdx.x & 63;

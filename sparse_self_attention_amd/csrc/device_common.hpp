@@ -73,4 +73,17 @@ __device__ inline uint32_t xcd_contiguous(uint32_t bid, uint32_t n) {
   return x * q + (x < r ? x : r) + pos;
 }
 
+// Workgroup id remap for the attention kernels: the logical range is cut into stripes of 8*S items
+// and XCD x takes the x-th run of S items of each stripe, so at any moment the eight XCDs work on
+// neighbouring items (one head's K/V stays hot in the shared last-level cache) while each XCD's own
+// L2 still sees runs of S adjacent items.  Past the last whole stripe the remainder is dealt out as
+// in xcd_contiguous.  A bijection of [0, n) for the round-robin dealing of workgroups to XCDs.
+__device__ inline uint32_t xcd_striped(uint32_t bid, uint32_t n, uint32_t S) {
+  const uint32_t x = bid & 7u, pos = bid >> 3;
+  const uint32_t C = 8u * S, K = n / C, k = pos / S;
+  if (k < K) return k * C + x * S + (pos - k * S);
+  const uint32_t R = n - K * C, q = R >> 3, r = R & 7u;
+  return K * C + x * q + (x < r ? x : r) + (pos - K * S);
+}
+
 }  // namespace sattn

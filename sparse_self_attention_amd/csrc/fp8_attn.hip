@@ -351,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   static_assert(NW >= ISETS, "one slot-row load per wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
 
-  const uint32_t unit = xcd_contiguous(blockIdx.x, n_units);
+  const uint32_t unit = xcd_striped(blockIdx.x, n_units, 128);
   const int g = (int)(unit % (uint32_t)G);
   const uint32_t bh = unit / (uint32_t)G;
   const int lane = threadIdx.x & 63;

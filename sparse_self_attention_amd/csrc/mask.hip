@@ -18,9 +18,10 @@
 //                 12 + 12 + 8 bit radix select finds the exact k-th largest (ties go to the lowest
 //                 key index).  If the band misses the cut or overflows LDS, the cut is found by
 //                 radix passes over the staged scores instead.  Threshold: block max + block sum
-//                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Keep flags live in
-//                 LDS bitmaps written by wave ballots; the ascending list is written from popcounts,
-//                 one block scan and mbcnt.
+//                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Scores are read
+//                 with 16-byte loads, 256 consecutive keys per wave and row.  Keep flags live in LDS
+//                 bitmaps written by wave ballots; the ascending list comes from popcounts, one block
+//                 scan and mbcnt, staged per 256-key chunk in LDS and written as contiguous runs.
 #include <math.h>
 
 #include "../../include/sattn.h"
@@ -263,11 +264,7 @@ __device__ inline float key_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-// Order-preserving key of the score of key j in this group (0 = no key: j >= Nk).
-__device__ inline uint32_t key_at(const float* srow, int j, int Nk) { return j < Nk ? order_key(srow[j]) : 0u; }
-
 constexpr int SEL_CAND = 4096;                                   // LDS candidates around the cut
-constexpr int SEL_UNROLL = 16;                                   // loads in flight per thread
 
 // In (digit-)bin search over hist[0..nb): the bin holding the kk-th largest element, counting from
 // the top.  Thread t owns bins nb-1-per*t ... (descending); writes found[0] = bin, found[1] = rank
@@ -323,20 +320,68 @@ __device__ inline void find_bin_pair(const int* hA, const int* hB, int nb, int k
   __syncthreads();
 }
 
-// One 1024-thread workgroup per group.  Keys j are visited as rows i of 1024: j = 1024 i + tid, so a
-// wave covers 64 consecutive keys of a row and its ballot is one 64-bit word pair of a bitmap.
+// One 1024-thread workgroup per group.  Keys are visited in rows of SEL_ROW = 4096: thread t reads keys
+// 4t .. 4t+3 of a row with one 16-byte load, so wave w covers the 256 consecutive keys of chunk
+// c = 16 i + w, i.e. keys [256 c, 256 c + 256).  A chunk's flags are its four wave ballots, one per element
+// e of the lanes' loads: bit l of ballot e flags key 256 c + 4 l + e.  Ballot e of chunk c is kept in
+// bitmap words 8c + 2e (lanes 0-31) and 8c + 2e + 1 (lanes 32-63).
 //  top-k:     the sample locates a band [key_lo, key_hi] around the cut; one pass (global) marks the
 //             keys above it in `strict` and copies the band's keys to LDS; an exact radix select on
 //             them resolves the cut; candidates above it join `strict`, ties at the cut go to `tie`.
 //             If the band misses the cut or overflows the LDS list, the cut and the flags are
 //             computed from global memory instead.
 //  threshold: pass 1 max, pass 2 sum of exp, pass 3 marks s >= lse + ln tau in `strict`.
-//  Compaction: popcounts of the bitmap words per (row, wave), one block scan, then each kept key
-//  writes its index at its rank; ties are taken lowest index first up to `need`.
+//  Compaction: popcounts of each chunk's bitmap words, one block scan, then each wave places the kept
+//  keys of its chunk at their ranks in an LDS staging row and writes the row out as one contiguous
+//  run; ties are taken lowest index first up to `need`.
+constexpr int SEL_KPT = 4;                          // keys per thread and row (one 16-byte load)
+constexpr int SEL_ROW = SEL_KPT * SEL_THREADS;      // keys per row
+constexpr int SEL_CHUNK = SEL_KPT * 64;             // keys per (row, wave)
+constexpr int SEL_BATCH = 8;                        // rows (16-byte loads) in flight per thread
+
 static inline size_t select_lds_bytes(int Nk, bool topk) {
-  const size_t rows = (size_t)(Nk + SEL_THREADS - 1) / SEL_THREADS;
-  const size_t words = rows * (SEL_THREADS / 32);
-  return 4 * ((topk ? 4096 : 0) + 2 * words + 2 * rows * SEL_WAVES + (topk ? 2 * SEL_CAND : 0));
+  const size_t rows = (size_t)(Nk + SEL_ROW - 1) / SEL_ROW;
+  const size_t chunks = rows * SEL_WAVES;
+  const size_t tail = topk ? 2 * SEL_CAND : (size_t)SEL_WAVES * SEL_CHUNK;   // candidates / output staging
+  return 4 * ((topk ? 4096 : 0) + 2 * 8 * chunks + 2 * chunks + tail);
+}
+
+// Order keys of keys i*SEL_ROW + 4*tid + e, e = 0..3 (0 past Nk).  Score rows are padded to a multiple of
+// 4 floats, so the 16-byte load of a partly valid quad stays inside its row.
+__device__ inline void keys4(const float* srow, int i, int tid, int Nk, uint32_t (&u)[SEL_KPT]) {
+  const int j = i * SEL_ROW + SEL_KPT * tid;
+  if (j < Nk) {
+    const f32x4 s = *(const f32x4*)(srow + j);
+#pragma unroll
+    for (int e = 0; e < SEL_KPT; ++e) u[e] = j + e < Nk ? order_key(s[e]) : 0u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < SEL_KPT; ++e) u[e] = 0u;
+  }
+}
+
+// Bitmap word and bit of key j.
+__device__ inline int flag_word(int j) { return 8 * (j >> 8) + 2 * (j & 3) + ((j >> 7) & 1); }
+__device__ inline uint32_t flag_bit(int j) { return 1u << ((j >> 2) & 31); }
+
+__device__ inline int mbcnt64(uint64_t b) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// Lanes 0..7 store the four ballots of chunk c, one word each.
+__device__ inline void store_ballots(uint32_t* bits, int c, const uint64_t (&b)[SEL_KPT], int lane) {
+  if (lane < 2 * SEL_KPT) {
+    const int e = lane >> 1;
+    const uint64_t w = e == 0 ? b[0] : e == 1 ? b[1] : e == 2 ? b[2] : b[3];
+    bits[8 * c + lane] = (lane & 1) ? (uint32_t)(w >> 32) : (uint32_t)w;
+  }
+}
+
+// Orders LDS writes of some lanes before LDS reads of other lanes of the same wave.
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // 2 workgroups per CU: at most 64 VGPRs (8 waves per SIMD).
@@ -355,15 +400,17 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   const int hh = blockIdx.x / G, g = blockIdx.x % G;
   const size_t unit = ((size_t)bh0 + hh) * G + g;
   const float* srow = scores + ((size_t)hh * G + g) * score_stride(Nk);
-  const int rows = (Nk + SEL_THREADS - 1) / SEL_THREADS;
-  const int words = rows * (SEL_THREADS / 32);
+  const int rows = (Nk + SEL_ROW - 1) / SEL_ROW;
+  const int chunks = rows * SEL_WAVES;
+  const int words = 8 * chunks;
   int* hist = sel_dyn;                                             // 4096 bins (top-k only)
   uint32_t* strict_bits = (uint32_t*)(sel_dyn + (TOPK ? 4096 : 0)); // words
   uint32_t* tie_bits = strict_bits + words;                        // words
-  int* cnt_s = (int*)(tie_bits + words);                           // rows * 16
-  int* cnt_t = cnt_s + rows * SEL_WAVES;                           // rows * 16
-  uint32_t* cand_key = (uint32_t*)(cnt_t + rows * SEL_WAVES);      // SEL_CAND (top-k only)
+  int* cnt_s = (int*)(tie_bits + words);                           // chunks
+  int* cnt_t = cnt_s + chunks;                                     // chunks
+  uint32_t* cand_key = (uint32_t*)(cnt_t + chunks);                // SEL_CAND (top-k); output staging after
   int* cand_j = (int*)(cand_key + SEL_CAND);                       // SEL_CAND (top-k only)
+  int* stage = (int*)cand_key + wave * SEL_CHUNK;                  // this wave's output staging row
 
   for (int w = tid; w < words; w += SEL_THREADS) { strict_bits[w] = 0u; tie_bits[w] = 0u; }
   int need = 0;
@@ -409,39 +456,43 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     if (tid == 0) ncand = 0;
     __syncthreads();
     // ---- 2. one pass: keys above the band -> strict bits; keys in it -> LDS candidates ----
-    int above_w = 0;   // keys above the band seen by this wave (lane 0)
-    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
-      uint32_t u[SEL_UNROLL];
+    int above_w = 0;   // keys above the band seen by this wave (uniform)
+    for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
+      uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
-      // ballots of the batch first, then one LDS atomic reserves the wave's candidate slots for it
-      uint64_t bc[SEL_UNROLL];
-      int nb = 0;
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) {
-        const int i = i0 + e;
-        const bool in = i < rows;
-        const uint64_t above = __builtin_amdgcn_ballot_w64(in && u[e] > key_hi);
-        bc[e] = __builtin_amdgcn_ballot_w64(in && u[e] != 0u && u[e] >= key_lo && u[e] <= key_hi);
-        nb += (int)__popcll(bc[e]);
-        if (in && lane == 0) {
-          const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
-          strict_bits[w0] = (uint32_t)above;
-          strict_bits[w0 + 1] = (uint32_t)(above >> 32);
-          above_w += __popcll(above);
+      for (int r = 0; r < SEL_BATCH; ++r) {
+        const int i = i0 + r;
+        if (i < rows) {
+          uint64_t ab[SEL_KPT], bc[SEL_KPT];
+          int nb = 0;
+#pragma unroll
+          for (int e = 0; e < SEL_KPT; ++e) {
+            const uint32_t x = u[r][e];
+            ab[e] = __builtin_amdgcn_ballot_w64(x > key_hi);
+            bc[e] = __builtin_amdgcn_ballot_w64(x != 0u && x >= key_lo && x <= key_hi);
+            nb += (int)__popcll(bc[e]);
+            above_w += (int)__popcll(ab[e]);
+          }
+          store_ballots(strict_bits, i * SEL_WAVES + wave, ab, lane);
+          if (nb > 0) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&ncand, nb);
+            base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+            for (int e = 0; e < SEL_KPT; ++e) {
+              if ((bc[e] >> lane) & 1u) {
+                const int pos = base + mbcnt64(bc[e]);
+                if (pos < SEL_CAND) {
+                  cand_key[pos] = u[r][e];
+                  cand_j[pos] = i * SEL_ROW + SEL_KPT * tid + e;
+                }
+              }
+              base += (int)__popcll(bc[e]);
+            }
+          }
         }
-      }
-      int base = 0;
-      if (lane == 0 && nb > 0) base = atomicAdd(&ncand, nb);
-      base = __builtin_amdgcn_readfirstlane(base);
-#pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) {
-        if ((bc[e] >> lane) & 1u) {
-          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc[e] >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bc[e], 0u));
-          if (pos < SEL_CAND) { cand_key[pos] = u[e]; cand_j[pos] = (i0 + e) * SEL_THREADS + tid; }
-        }
-        base += (int)__popcll(bc[e]);
       }
     }
     if (lane == 0) ired[wave] = above_w;
@@ -478,8 +529,8 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       for (int x = tid; x < nc; x += SEL_THREADS) {
         const uint32_t u = cand_key[x];
         const int jj = cand_j[x];
-        if (u > prefix) atomicOr(&strict_bits[jj >> 5], 1u << (jj & 31));
-        else if (u == prefix) atomicOr(&tie_bits[jj >> 5], 1u << (jj & 31));
+        if (u > prefix) atomicOr(&strict_bits[flag_word(jj)], flag_bit(jj));
+        else if (u == prefix) atomicOr(&tie_bits[flag_word(jj)], flag_bit(jj));
       }
       __syncthreads();
     } else {
@@ -493,14 +544,15 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         for (int bb = tid; bb < nb; bb += SEL_THREADS) hist[bb] = 0;
         if (tid == 0) { found[0] = 0; found[1] = 1; }
         __syncthreads();
-        for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
-          uint32_t u[SEL_UNROLL];
+        for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
+          uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-          for (int e = 0; e < SEL_UNROLL; ++e)
-            u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+          for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
 #pragma unroll
-          for (int e = 0; e < SEL_UNROLL; ++e)
-            if (u[e] != 0u && (u[e] & pmask) == prefix) atomicAdd(&hist[(u[e] >> sh) & (nb - 1)], 1);
+          for (int r = 0; r < SEL_BATCH; ++r)
+#pragma unroll
+            for (int e = 0; e < SEL_KPT; ++e)
+              if (u[r][e] != 0u && (u[r][e] & pmask) == prefix) atomicAdd(&hist[(u[r][e] >> sh) & (nb - 1)], 1);
         }
         __syncthreads();
         find_bin(hist, nb, kk, wsum, found);
@@ -511,58 +563,59 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       }
       need = kk;
       for (int i = 0; i < rows; ++i) {
-        const uint32_t u = key_at(srow, i * SEL_THREADS + tid, Nk);
-        const uint64_t st = __builtin_amdgcn_ballot_w64(u > prefix);
-        const uint64_t ti = __builtin_amdgcn_ballot_w64(u == prefix && u != 0u);
-        if (lane == 0) {
-          const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
-          strict_bits[w0] = (uint32_t)st;
-          strict_bits[w0 + 1] = (uint32_t)(st >> 32);
-          tie_bits[w0] = (uint32_t)ti;
-          tie_bits[w0 + 1] = (uint32_t)(ti >> 32);
+        uint32_t u[SEL_KPT];
+        keys4(srow, i, tid, Nk, u);
+        uint64_t st[SEL_KPT], ti[SEL_KPT];
+#pragma unroll
+        for (int e = 0; e < SEL_KPT; ++e) {
+          st[e] = __builtin_amdgcn_ballot_w64(u[e] > prefix);
+          ti[e] = __builtin_amdgcn_ballot_w64(u[e] == prefix && u[e] != 0u);
         }
+        store_ballots(strict_bits, i * SEL_WAVES + wave, st, lane);
+        store_ballots(tie_bits, i * SEL_WAVES + wave, ti, lane);
       }
       __syncthreads();
     }
   } else {
     __syncthreads();
     float m = -INFINITY;
-    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
-      uint32_t u[SEL_UNROLL];
+    for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
+      uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e)
-        if (u[e] != 0u) m = fmaxf(m, key_to_float(u[e]));
+      for (int r = 0; r < SEL_BATCH; ++r)
+#pragma unroll
+        for (int e = 0; e < SEL_KPT; ++e)
+          if (u[r][e] != 0u) m = fmaxf(m, key_to_float(u[r][e]));
     }
     m = block_max(m, fred);
     float ssum = 0.0f;
-    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
-      uint32_t u[SEL_UNROLL];
+    for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
+      uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e)
-        if (u[e] != 0u) ssum += expf(key_to_float(u[e]) - m);
+      for (int r = 0; r < SEL_BATCH; ++r)
+#pragma unroll
+        for (int e = 0; e < SEL_KPT; ++e)
+          if (u[r][e] != 0u) ssum += expf(key_to_float(u[r][e]) - m);
     }
     ssum = block_sum(ssum, fred);
     const float t = m + logf(ssum) + log_tau;   // log_tau = -inf keeps every key
     // keep s_j >= t  <=>  order_key(s_j) >= order_key(t), i.e. u > cut with cut = key(t) - 1
     const uint32_t cut = ((isinf(t) && t < 0.0f) ? 1u : order_key(t)) - 1u;
-    for (int i0 = 0; i0 < rows; i0 += SEL_UNROLL) {
-      uint32_t u[SEL_UNROLL];
+    for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
+      uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) u[e] = (i0 + e < rows) ? key_at(srow, (i0 + e) * SEL_THREADS + tid, Nk) : 0u;
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
 #pragma unroll
-      for (int e = 0; e < SEL_UNROLL; ++e) {
-        const int i = i0 + e;
-        if (i < rows) {
-          const uint64_t st = __builtin_amdgcn_ballot_w64(u[e] > cut);
-          if (lane == 0) {
-            const int w0 = (i * SEL_THREADS + wave * 64) >> 5;
-            strict_bits[w0] = (uint32_t)st;
-            strict_bits[w0 + 1] = (uint32_t)(st >> 32);
-          }
+      for (int r = 0; r < SEL_BATCH; ++r) {
+        if (i0 + r < rows) {
+          uint64_t st[SEL_KPT];
+#pragma unroll
+          for (int e = 0; e < SEL_KPT; ++e) st[e] = __builtin_amdgcn_ballot_w64(u[r][e] > cut);
+          store_ballots(strict_bits, (i0 + r) * SEL_WAVES + wave, st, lane);
         }
       }
     }
@@ -570,18 +623,22 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   }
 
   // ---- compaction in ascending key order ----
-  for (int x = tid; x < rows * SEL_WAVES; x += SEL_THREADS) {
-    const int w0 = x * 2;   // (row, wave) entry x owns bitmap words 2x, 2x+1
-    cnt_s[x] = __popc(strict_bits[w0]) + __popc(strict_bits[w0 + 1]);
-    cnt_t[x] = __popc(tie_bits[w0]) + __popc(tie_bits[w0 + 1]);
+  for (int x = tid; x < chunks; x += SEL_THREADS) {
+    int a = 0, b = 0;
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+      a += __popc(strict_bits[8 * x + k2]);
+      b += __popc(tie_bits[8 * x + k2]);
+    }
+    cnt_s[x] = a;
+    cnt_t[x] = b;
   }
   __syncthreads();
-  const int nent = rows * SEL_WAVES;
-  const int E = (nent + SEL_THREADS - 1) / SEL_THREADS;
+  const int E = (chunks + SEL_THREADS - 1) / SEL_THREADS;
   int ls = 0, lt = 0;
   for (int e = 0; e < E; ++e) {
     const int x = tid * E + e;
-    if (x < nent) { ls += cnt_s[x]; lt += cnt_t[x]; }
+    if (x < chunks) { ls += cnt_s[x]; lt += cnt_t[x]; }
   }
   int tot_s, tot_t;
   const int base_s = block_excl_scan(ls, wsum, tot_s);
@@ -590,7 +647,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     int rs = base_s, rt = base_t;
     for (int e = 0; e < E; ++e) {
       const int x = tid * E + e;
-      if (x < nent) {
+      if (x < chunks) {
         const int a = cnt_s[x], b = cnt_t[x];
         cnt_s[x] = rs; cnt_t[x] = rt;
         rs += a; rt += b;
@@ -601,26 +658,47 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   int32_t* out = idx + unit * (size_t)cap;
   const int kept = tot_s + min(tot_t, need);
   if (kept > 0) {
-#pragma unroll 4
     for (int i = 0; i < rows; ++i) {
       const int x = i * SEL_WAVES + wave;
-      const uint64_t bs = (uint64_t)strict_bits[2 * x] | ((uint64_t)strict_bits[2 * x + 1] << 32);
-      const uint64_t bt = (uint64_t)tie_bits[2 * x] | ((uint64_t)tie_bits[2 * x + 1] << 32);
-      const bool st = (bs >> lane) & 1u;
-      const bool tie = ((bt >> lane) & 1u) && need > 0;
-      const int before_s = cnt_s[x] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u));
-      const int before_t = cnt_t[x] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
-      const bool keep = st || (tie && before_t < need);
-      const int pos = before_s + min(before_t, need);
-      if (keep && pos < cap) out[pos] = i * SEL_THREADS + tid;
+      uint64_t bs[SEL_KPT], bt[SEL_KPT];
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e) {
+        bs[e] = (uint64_t)strict_bits[8 * x + 2 * e] | ((uint64_t)strict_bits[8 * x + 2 * e + 1] << 32);
+        bt[e] = (uint64_t)tie_bits[8 * x + 2 * e] | ((uint64_t)tie_bits[8 * x + 2 * e + 1] << 32);
+      }
+      const int cs = cnt_s[x], ct = cnt_t[x];
+      int before_s = cs, before_t = ct, ns = 0, nt = 0;   // keys before this lane's first key; chunk totals
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e) {
+        before_s += mbcnt64(bs[e]);
+        before_t += mbcnt64(bt[e]);
+        ns += (int)__popcll(bs[e]);
+        nt += (int)__popcll(bt[e]);
+      }
+      const int p0 = cs + min(ct, need);                      // output slot of the chunk's first kept key
+      const int n_x = cs + ns + min(ct + nt, need) - p0;      // kept keys of the chunk
+      if (n_x == 0) continue;
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e) {
+        const int st = (int)((bs[e] >> lane) & 1u), tie = (int)((bt[e] >> lane) & 1u);
+        if (st || (tie && before_t < need)) stage[before_s + min(before_t, need) - p0] = x * SEL_CHUNK + SEL_KPT * lane + e;
+        before_s += st;
+        before_t += tie;
+      }
+      wave_sync();
+      for (int m = lane; m < n_x; m += 64)
+        if (p0 + m < cap) out[p0 + m] = stage[m];
+      wave_sync();
     }
     if (tid == 0) counts[unit] = min(kept, cap);
   } else {
     // threshold mode with no key at the cut: keep the arg-max, lowest index on ties
     uint32_t best = 0;
     for (int i = 0; i < rows; ++i) {
-      const uint32_t u = key_at(srow, i * SEL_THREADS + tid, Nk);
-      best = u > best ? u : best;
+      uint32_t u[SEL_KPT];
+      keys4(srow, i, tid, Nk, u);
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e) best = u[e] > best ? u[e] : best;
     }
     for (int off = 32; off > 0; off >>= 1) {
       const uint32_t o = (uint32_t)__shfl_xor((int)best, off);
@@ -633,8 +711,11 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     __syncthreads();
     int jmin = 0x7fffffff;
     for (int i = 0; i < rows; ++i) {
-      const uint32_t u = key_at(srow, i * SEL_THREADS + tid, Nk);
-      if (u == bmax && u != 0u) jmin = min(jmin, i * SEL_THREADS + tid);
+      uint32_t u[SEL_KPT];
+      keys4(srow, i, tid, Nk, u);
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e)
+        if (u[e] == bmax && u[e] != 0u) jmin = min(jmin, i * SEL_ROW + SEL_KPT * tid + e);
     }
     jmin = block_min_int(jmin, ired);
     if (tid == 0) {
