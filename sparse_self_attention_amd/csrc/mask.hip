@@ -21,7 +21,7 @@
 //                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Scores are read
 //                 with 16-byte loads, 256 consecutive keys per wave and row.  Keep flags live in LDS
 //                 bitmaps written by wave ballots; the ascending list comes from popcounts, one block
-//                 scan and mbcnt, staged per 256-key chunk in LDS and written as contiguous runs.
+//                 scan and mbcnt.
 #include <math.h>
 
 #include "../../include/sattn.h"
@@ -331,9 +331,9 @@ __device__ inline void find_bin_pair(const int* hA, const int* hB, int nb, int k
 //             If the band misses the cut or overflows the LDS list, the cut and the flags are
 //             computed from global memory instead.
 //  threshold: pass 1 max, pass 2 sum of exp, pass 3 marks s >= lse + ln tau in `strict`.
-//  Compaction: popcounts of each chunk's bitmap words, one block scan, then each wave places the kept
-//  keys of its chunk at their ranks in an LDS staging row and writes the row out as one contiguous
-//  run; ties are taken lowest index first up to `need`.
+//  Compaction: popcounts of each chunk's bitmap words, one block scan, then each kept key writes its
+//  index at its rank (mbcnt over the chunk's four ballots); ties are taken lowest index first up to
+//  `need`.
 constexpr int SEL_KPT = 4;                          // keys per thread and row (one 16-byte load)
 constexpr int SEL_ROW = SEL_KPT * SEL_THREADS;      // keys per row
 constexpr int SEL_CHUNK = SEL_KPT * 64;             // keys per (row, wave)
@@ -342,8 +342,7 @@ constexpr int SEL_BATCH = 8;                        // rows (16-byte loads) in f
 static inline size_t select_lds_bytes(int Nk, bool topk) {
   const size_t rows = (size_t)(Nk + SEL_ROW - 1) / SEL_ROW;
   const size_t chunks = rows * SEL_WAVES;
-  const size_t tail = topk ? 2 * SEL_CAND : (size_t)SEL_WAVES * SEL_CHUNK;   // candidates / output staging
-  return 4 * ((topk ? 4096 : 0) + 2 * 8 * chunks + 2 * chunks + tail);
+  return 4 * ((topk ? 4096 : 0) + 2 * 8 * chunks + 2 * chunks + (topk ? 2 * SEL_CAND : 0));
 }
 
 // Order keys of keys i*SEL_ROW + 4*tid + e, e = 0..3 (0 past Nk).  Score rows are padded to a multiple of
@@ -377,13 +376,6 @@ __device__ inline void store_ballots(uint32_t* bits, int c, const uint64_t (&b)[
   }
 }
 
-// Orders LDS writes of some lanes before LDS reads of other lanes of the same wave.
-__device__ inline void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // 2 workgroups per CU: at most 64 VGPRs (8 waves per SIMD).
 template <bool TOPK>
 __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
@@ -408,9 +400,8 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   uint32_t* tie_bits = strict_bits + words;                        // words
   int* cnt_s = (int*)(tie_bits + words);                           // chunks
   int* cnt_t = cnt_s + chunks;                                     // chunks
-  uint32_t* cand_key = (uint32_t*)(cnt_t + chunks);                // SEL_CAND (top-k); output staging after
+  uint32_t* cand_key = (uint32_t*)(cnt_t + chunks);                // SEL_CAND (top-k only)
   int* cand_j = (int*)(cand_key + SEL_CAND);                       // SEL_CAND (top-k only)
-  int* stage = (int*)cand_key + wave * SEL_CHUNK;                  // this wave's output staging row
 
   for (int w = tid; w < words; w += SEL_THREADS) { strict_bits[w] = 0u; tie_bits[w] = 0u; }
   int need = 0;
@@ -666,29 +657,21 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         bs[e] = (uint64_t)strict_bits[8 * x + 2 * e] | ((uint64_t)strict_bits[8 * x + 2 * e + 1] << 32);
         bt[e] = (uint64_t)tie_bits[8 * x + 2 * e] | ((uint64_t)tie_bits[8 * x + 2 * e + 1] << 32);
       }
-      const int cs = cnt_s[x], ct = cnt_t[x];
-      int before_s = cs, before_t = ct, ns = 0, nt = 0;   // keys before this lane's first key; chunk totals
+      // keys of the chunk before this lane's first key, then this lane's four keys in order
+      int before_s = __builtin_amdgcn_readfirstlane(cnt_s[x]), before_t = __builtin_amdgcn_readfirstlane(cnt_t[x]);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) {
         before_s += mbcnt64(bs[e]);
         before_t += mbcnt64(bt[e]);
-        ns += (int)__popcll(bs[e]);
-        nt += (int)__popcll(bt[e]);
       }
-      const int p0 = cs + min(ct, need);                      // output slot of the chunk's first kept key
-      const int n_x = cs + ns + min(ct + nt, need) - p0;      // kept keys of the chunk
-      if (n_x == 0) continue;
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) {
         const int st = (int)((bs[e] >> lane) & 1u), tie = (int)((bt[e] >> lane) & 1u);
-        if (st || (tie && before_t < need)) stage[before_s + min(before_t, need) - p0] = x * SEL_CHUNK + SEL_KPT * lane + e;
+        const int pos = before_s + min(before_t, need);
+        if ((st || (tie && before_t < need)) && pos < cap) out[pos] = x * SEL_CHUNK + SEL_KPT * lane + e;
         before_s += st;
         before_t += tie;
       }
-      wave_sync();
-      for (int m = lane; m < n_x; m += 64)
-        if (p0 + m < cap) out[p0 + m] = stage[m];
-      wave_sync();
     }
     if (tid == 0) counts[unit] = min(kept, cap);
   } else {
