@@ -228,9 +228,12 @@ def main():
         "gathered_GBps_fwd": round(float(cnt_h.sum()) * 2 * w.dim * 2 / (fwd_avg * 1e-3) / 1e9, 1),
     }
     # dominant kernel: the sparse forward (one launch per step)
+    traffic = recorded_traffic(w.name)
     rec["roofline"] = {"bound": "mfma", "kernel": f"attn_fwd_lean<{w.dim},sparse,bf16>",
                        "achieved": round(fwd_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                       "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(w.name)}
+                       "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    # the gather path beyond L2: the recorded per-launch fetch+write bytes over this run's launch time
+    rec["beyond_l2_GBps_fwd"] = round(traffic / (fwd_avg * 1e-3) / 1e9, 1) if traffic else None
     if args.copy_calibration_mib > 0:
         src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -84,7 +84,7 @@ def test_forward_validation(lib, kw, code):
 MASK_CASES = [
     (dict(q=P(0)), ERR_NULL), (dict(counts=P(0)), ERR_NULL),
     (dict(H=0), ERR_SHAPE), (dict(D=32), ERR_UNSUPPORTED), (dict(group=24), ERR_UNSUPPORTED),
-    (dict(Nk=200000), ERR_UNSUPPORTED),
+    (dict(Nk=200000), ERR_UNSUPPORTED), (dict(Nk=131073, topk=16), ERR_UNSUPPORTED),
     (dict(mode=2), ERR_ARG), (dict(topk=0), ERR_ARG), (dict(topk=129), ERR_ARG), (dict(cap=15), ERR_ARG),
     (dict(mode=1, thresh=-0.1, cap=128), ERR_ARG), (dict(mode=1, thresh=1.5, cap=128), ERR_ARG),
     (dict(mode=1, thresh=float("nan"), cap=128), ERR_ARG), (dict(mode=1, thresh=0.1, cap=127), ERR_ARG),

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import check_mask_sets, f64, scale_of, to_device_bf16, workload
+from gpu_util import check_lse, check_mask_sets, check_out, f64, scale_of, to_device_bf16, workload
 from synth import inputs
 
 pytestmark = pytest.mark.gpu
@@ -116,3 +116,29 @@ def test_crowded_cut_bin_uses_global_passes(sattn):
     kb = np.broadcast_to(kb[:, :, :1], (1, 1, Nk, D)).copy()
     idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=20000)
     assert np.all(cnt == 20000) and np.all(idx == np.arange(20000))
+
+
+def test_maximum_key_count(sattn):
+    """Nk at the mask's limit (131072 keys: the longest sample row the select's LDS takes, the largest
+    bitmaps): top-k and threshold lists of both groups against the oracle, then the forward on the
+    top-k lists against the oracle."""
+    rng = np.random.default_rng(131072)
+    D, group, Nq, Nk = 64, 128, 256, 131072
+    qb = _bits(rng, (1, 1, Nq, D), 2.0)
+    kb = _bits(rng, (1, 1, Nk, D))
+    vb = _bits(rng, (1, 1, Nk, D))
+    units = _all_units(1, 1, 2)
+    kk = Nk // 5
+    ref = oracle.mask_ref(f64(qb), f64(kb), group, "topk", topk=kk)
+    idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=kk)
+    check_mask_sets(idx, cnt, ref, units, "max Nk topk", exact_counts=True)
+    ref_t = oracle.mask_ref(f64(qb), f64(kb), group, "thresh", thresh=1e-5)
+    idx_t, cnt_t = _gpu_mask(sattn, qb, kb, group, thresh=1e-5)
+    check_mask_sets(idx_t, cnt_t, ref_t, units, "max Nk thresh", exact_counts=False)
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+    out, lse = sattn.forward(q, k, v, ti, tc, group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attention_ref(f64(qb), f64(kb), f64(vb), idx, cnt, group, scale_of(D))
+    check_out(out.cpu().numpy(), ro, "max Nk forward")
+    check_lse(lse.cpu().numpy(), rl, "max Nk forward")
