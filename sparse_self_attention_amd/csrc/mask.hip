@@ -346,7 +346,7 @@ static inline size_t select_lds_bytes(int Nk, bool topk) {
 }
 
 // Order keys of keys i*SEL_ROW + 4*tid + e, e = 0..3 (0 past Nk).  Score rows are padded to a multiple of
-// 4 floats, so the 16-byte load of a partly valid quad stays inside its row.
+// 32 floats, so the 16-byte load of a partly valid quad stays inside its row.
 __device__ inline void keys4(const float* srow, int i, int tid, int Nk, uint32_t (&u)[SEL_KPT]) {
   const int j = i * SEL_ROW + SEL_KPT * tid;
   if (j < Nk) {
