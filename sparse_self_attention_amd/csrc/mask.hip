@@ -116,6 +116,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   constexpr int TILE = 32 * RB;
   constexpr int ROWDIV = 16 / NC;
   __shared__ __attribute__((aligned(1024))) char ktile[2 * TILE];
+  // this workgroup's samples (SC_KT * 32 / SAMPLE_STEP per group), stored as whole runs at the end
+  constexpr int SPW = SC_KT * 32 / SAMPLE_STEP;
+  __shared__ float ssamp[128 * SPW];
   auto swz = [](int row) { return (row / ROWDIV) % NC; };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -188,10 +191,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         if (g < G) {
           const float sv = acc[r] * scale;
           sbase[(size_t)g * stride + j] = sv;
-          if (sampler) pbase[(size_t)g * sstride + j / SAMPLE_STEP] = sv;
+          if (sampler) ssamp[(g - gq * 128) * SPW + (j - jbase) / SAMPLE_STEP] = sv;
         }
       }
     }
+  }
+  __syncthreads();   // every wave's samples are in LDS
+  const int p0 = jbase / SAMPLE_STEP, plen = sample_len(Nk);
+  for (int e = (int)threadIdx.x; e < 128 * SPW; e += 256) {
+    const int g = gq * 128 + e / SPW, p = p0 + e % SPW;
+    if (g < G && p < plen) pbase[(size_t)g * sstride + p] = ssamp[e];
   }
 }
 
