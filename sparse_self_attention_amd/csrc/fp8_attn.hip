@@ -73,58 +73,83 @@ __device__ inline uint32_t bf16_bits_rne_f64(double x) {
 }
 
 // Per (head, block): bf16 block means (exact fp64 sum of the bf16 tokens, divided by the token
-// count) and the per-channel max |v - mean| of the block.
+// count) and the per-channel max |v - mean| of the block.  Thread t reads 16-byte pieces (8 channels)
+// of every RPT-th token row; the fp64 sums are exact, so their order does not matter.
 template <int D>
 __global__ __launch_bounds__(256) void k_vs_stats(const uint16_t* __restrict__ v, int Nk, int NB,
                                                   uint16_t* __restrict__ mean_ws, float* __restrict__ bmax_ws) {
-  constexpr int TPC = 256 / D;            // threads per channel
-  constexpr int TOK = VS_BLOCK / TPC;     // tokens per thread
-  __shared__ double part[256];
-  __shared__ float pmax[256];
+  constexpr int CG = D / 8;               // 16-byte channel groups per row
+  constexpr int RPT = 256 / CG;           // token rows read at once
+  constexpr int TOK = VS_BLOCK / RPT;     // tokens per thread
+  __shared__ double part[RPT][D];
+  __shared__ float pmax[RPT][D];
+  __shared__ float meanf[D];
   const int blk = (int)(blockIdx.x % (uint32_t)NB);
   const size_t bh = blockIdx.x / (uint32_t)NB;
-  const int d = threadIdx.x % D, pi = threadIdx.x / D;
+  const int cg = threadIdx.x % CG, tr = threadIdx.x / CG;
   const int nb0 = blk * VS_BLOCK;
   const int ntok = min(VS_BLOCK, Nk - nb0);
-  const uint16_t* vb = v + (bh * Nk + nb0) * D + d;
-  float x[TOK];
+  const uint16_t* vb = v + (bh * Nk + nb0) * D + 8 * cg;
+  u32x4 w[TOK];
 #pragma unroll
   for (int i = 0; i < TOK; ++i) {
-    const int t = pi * TOK + i;
-    x[i] = t < ntok ? bf16_bits_to_float(vb[(size_t)t * D]) : 0.0f;
+    const int t = tr + i * RPT;
+    w[i] = t < ntok ? *(const u32x4*)(vb + (size_t)t * D) : u32x4{0u, 0u, 0u, 0u};
   }
-  double s = 0.0;
+  auto elem = [&](int i, int c) { return bf16_bits_to_float((w[i][c >> 1] >> (16 * (c & 1))) & 0xffffu); };
 #pragma unroll
-  for (int i = 0; i < TOK; ++i) s += (double)x[i];
-  part[threadIdx.x] = s;
+  for (int c = 0; c < 8; ++c) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) s += (double)elem(i, c);
+    part[tr][8 * cg + c] = s;
+  }
   __syncthreads();
-  double tot = 0.0;
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    double tot = 0.0;
 #pragma unroll
-  for (int p = 0; p < TPC; ++p) tot += part[p * D + d];
-  const uint32_t mb = bf16_bits_rne_f64(tot / (double)ntok);
-  const float mf = bf16_bits_to_float(mb);
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < TOK; ++i)
-    if (pi * TOK + i < ntok) m = fmaxf(m, fabsf(x[i] - mf));
-  pmax[threadIdx.x] = m;
-  __syncthreads();
-  if (pi == 0) {
-    float a = pmax[d];
-#pragma unroll
-    for (int p = 1; p < TPC; ++p) a = fmaxf(a, pmax[p * D + d]);
+    for (int r = 0; r < RPT; ++r) tot += part[r][d];
+    const uint32_t mb = bf16_bits_rne_f64(tot / (double)ntok);
+    meanf[d] = bf16_bits_to_float(mb);
     mean_ws[(bh * NB + blk) * D + d] = (uint16_t)mb;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float mf = meanf[8 * cg + c];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i)
+      if (tr + i * RPT < ntok) m = fmaxf(m, fabsf(elem(i, c) - mf));
+    pmax[tr][8 * cg + c] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float a = pmax[0][d];
+#pragma unroll
+    for (int r = 1; r < RPT; ++r) a = fmaxf(a, pmax[r][d]);
     bmax_ws[(bh * NB + blk) * D + d] = a;
   }
 }
 
-// Per head: channel scale 2^e, the smallest power of two with 448 * 2^e >= max |residual|.
+// Per head: channel scale 2^e, the smallest power of two with 448 * 2^e >= max |residual|.  VS_SLICES
+// threads per channel take every VS_SLICES-th block; the slice maxima meet in LDS.
+constexpr int VS_SLICES = 8;
 template <int D>
-__global__ __launch_bounds__(D) void k_vs_scale(const float* __restrict__ bmax_ws, int NB, float* __restrict__ vscale) {
+__global__ __launch_bounds__(D * VS_SLICES) void k_vs_scale(const float* __restrict__ bmax_ws, int NB,
+                                                           float* __restrict__ vscale) {
+  __shared__ float part[VS_SLICES][D];
   const size_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x % D, sl = threadIdx.x / D;
   float a = 0.0f;
-  for (int b = 0; b < NB; ++b) a = fmaxf(a, bmax_ws[(bh * NB + b) * D + d]);
+  for (int b = sl; b < NB; b += VS_SLICES) a = fmaxf(a, bmax_ws[(bh * NB + b) * D + d]);
+  part[sl][d] = a;
+  __syncthreads();
+  if (sl != 0) return;
+#pragma unroll
+  for (int k = 1; k < VS_SLICES; ++k) a = fmaxf(a, part[k][d]);
   int e = 0;
   if (a > 0.0f) {
     int x;
@@ -186,12 +211,12 @@ int launch_vsmooth(const VsmoothArgs& a) {
   const uint16_t* v = (const uint16_t*)a.v;
   if (a.D == 128) {
     hipLaunchKernelGGL(k_vs_stats<128>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, mean_ws, bmax_ws);
-    hipLaunchKernelGGL(k_vs_scale<128>, dim3(BH), dim3(128), 0, st, bmax_ws, NB, a.vscale);
+    hipLaunchKernelGGL(k_vs_scale<128>, dim3(BH), dim3(128 * VS_SLICES), 0, st, bmax_ws, NB, a.vscale);
     hipLaunchKernelGGL(k_vs_codes<128>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, nbp, mean_ws, a.vscale,
                        a.codes, (uint16_t*)a.vmean);
   } else {
     hipLaunchKernelGGL(k_vs_stats<64>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, mean_ws, bmax_ws);
-    hipLaunchKernelGGL(k_vs_scale<64>, dim3(BH), dim3(64), 0, st, bmax_ws, NB, a.vscale);
+    hipLaunchKernelGGL(k_vs_scale<64>, dim3(BH), dim3(64 * VS_SLICES), 0, st, bmax_ws, NB, a.vscale);
     hipLaunchKernelGGL(k_vs_codes<64>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, nbp, mean_ws, a.vscale,
                        a.codes, (uint16_t*)a.vmean);
   }
