@@ -14,6 +14,7 @@ roofline of the dominant kernel and the fp64 CPU oracle timed on a bounded sampl
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -37,6 +38,8 @@ def parse():
     p.add_argument("--steps", type=int, default=8)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="long_70200")
+    p.add_argument("--density", type=float, default=None,
+                   help="top-k fraction of the keys kept per group instead of the workload's own (a sweep point)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=0, help="oracle units to time (default: 4 per core)")
     p.add_argument("--kernel-only", action="store_true",
@@ -153,6 +156,11 @@ def main():
         build.build()
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
+    if args.density is not None:
+        if w.mode != "topk" or not 0.0 < args.density <= 1.0:
+            print("--density needs a top-k workload and a fraction in (0, 1]", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, keep=args.density)
     t_gen = time.perf_counter()
     qb, kb, vb = inputs.generate(w)
     t_gen = time.perf_counter() - t_gen

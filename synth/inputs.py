@@ -168,7 +168,7 @@ def generate(w: Workload, heads: Optional[Sequence[int]] = None) -> tuple:
             q[b, j], k[b, j], v[b, j] = generate_head(w, b, h)
     if w.voxel is not None:
         perm = voxel_order(w.grid_k, w.voxel)
-        q, k, v = q[:, :, perm], k[:, :, perm], v[:, :, perm]
+        q, k, v = (np.ascontiguousarray(x[:, :, perm]) for x in (q, k, v))
     return q, k, v
 
 
