@@ -8,7 +8,8 @@
 //
 // Mapping onto CDNA4
 // ------------------
-//  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32) of the group.
+//  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32) of the group.  A
+//    group wider than 128 rows runs as one launch per 128-row slice, at most four waves each.
 //    Workgroup ids are striped over the XCDs in runs of 128 units, so the eight XCDs work on
 //    neighbouring groups of one head at a time (its K/V stay in the last-level cache).
 //  * Key blocks of 32 kept keys.  The block's K and V rows are gathered from HBM straight
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap,
     int Nq, int Nk, int group, int G, float scale_log2, void* __restrict__ out, float* __restrict__ lse,
     uint32_t n_units, const float* __restrict__ lse_in, const float* __restrict__ out_prev,
-    float* __restrict__ fresh) {
+    float* __restrict__ fresh, int row0) {
   using L = FwdLayout<D, BKL>;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_BYTES];
@@ -88,10 +89,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hi = lane >> 5;
   const int ql = lane & 31;
-  const int r0 = g * group;
-  const int rows_in_group = min(group, Nq - r0);
+  // this launch covers rows [row0, row0 + 32 NW) of the group (groups wider than 128 rows run as several
+  // launches of at most four waves)
+  const int r0 = g * group + row0;
+  const int rows_here = min(min(group - row0, NW * 32), Nq - r0);
+  if (rows_here <= 0) return;   // the partial last group may end before this launch's rows
   const int wrow = wave * 32 + ql;
-  const bool row_valid = wrow < rows_in_group;
+  const bool row_valid = wrow < rows_here;
 
   int c;
   if (DENSE) {
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 }
 
 template <int D, int NW, bool DENSE, bool DELTA>
-static int launch_lean_t(const FwdArgs& a) {
+static int launch_lean_t(const FwdArgs& a, int row0) {
   const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
   const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
@@ -292,27 +296,33 @@ static int launch_lean_t(const FwdArgs& a) {
     hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
-                       a.fresh);
+                       a.fresh, row0);
   else
     hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
-                       a.fresh);
+                       a.fresh, row0);
   return (int)hipGetLastError();
 }
 
+// Groups of up to 128 rows: one launch, one wave per 32 rows.  Wider groups: one launch per 128-row slice
+// of every group, four waves each (two for a slice of at most 64 rows).  A six- or eight-wave workgroup
+// would gather each list once, but it places its waves two deep on some SIMDs and only one such
+// workgroup then fits per CU at this kernel's register budget (1.4 waves per SIMD against 2.8).
 template <int D, bool DELTA>
 static int launch_sparse_d(const FwdArgs& a) {
-  const int waves = (a.group + 31) / 32;
-  if (waves <= 2) return launch_lean_t<D, 2, false, DELTA>(a);
-  if (waves <= 4) return launch_lean_t<D, 4, false, DELTA>(a);
-  if (waves <= 6) return launch_lean_t<D, 6, false, DELTA>(a);
-  return launch_lean_t<D, 8, false, DELTA>(a);
+  for (int row0 = 0; row0 < a.group; row0 += 128) {
+    const int rows = a.group - row0 < 128 ? a.group - row0 : 128;
+    const int waves = (rows + 31) / 32;
+    const int err = waves <= 2 ? launch_lean_t<D, 2, false, DELTA>(a, row0) : launch_lean_t<D, 4, false, DELTA>(a, row0);
+    if (err) return err;
+  }
+  return 0;
 }
 
 template <int D>
 static int launch_fwd_d(const FwdArgs& a) {
-  if (a.dense) return launch_lean_t<D, 4, true, false>(a);
+  if (a.dense) return launch_lean_t<D, 4, true, false>(a, 0);
   return a.delta ? launch_sparse_d<D, true>(a) : launch_sparse_d<D, false>(a);
 }
 
