@@ -9,7 +9,7 @@
 // Mapping onto CDNA4
 // ------------------
 //  * One workgroup per (batch, head, group); wave w owns query rows [32w, 32w+32) of the group.  A
-//    group wider than 128 rows runs as one launch per 128-row slice, at most four waves each.
+//    group wider than 128 rows runs as equal slices of at most 128 rows, one launch per slice.
 //    Workgroup ids are striped over the XCDs in runs of 128 units, so the eight XCDs work on
 //    neighbouring groups of one head at a time (its K/V stay in the last-level cache).
 //  * Key blocks of 32 kept keys.  The block's K and V rows are gathered from HBM straight
@@ -305,16 +305,19 @@ static int launch_lean_t(const FwdArgs& a, int row0) {
   return (int)hipGetLastError();
 }
 
-// Groups of up to 128 rows: one launch, one wave per 32 rows.  Wider groups: one launch per 128-row slice
-// of every group, four waves each (two for a slice of at most 64 rows).  A six- or eight-wave workgroup
-// would gather each list once, but it places its waves two deep on some SIMDs and only one such
-// workgroup then fits per CU at this kernel's register budget (1.4 waves per SIMD against 2.8).
+// Groups of up to 128 rows: one launch, one wave per 32 rows.  Wider groups: the rows are cut into equal
+// slices of at most 128 (192 -> 2 x 96, 256 -> 2 x 128), one launch per slice of every group.  A six- or
+// eight-wave workgroup would gather each list once, but it places its waves two deep on some SIMDs and
+// only one such workgroup then fits per CU at this kernel's register budget (1.4 waves per SIMD against
+// 2.8).
 template <int D, bool DELTA>
 static int launch_sparse_d(const FwdArgs& a) {
-  for (int row0 = 0; row0 < a.group; row0 += 128) {
-    const int rows = a.group - row0 < 128 ? a.group - row0 : 128;
-    const int waves = (rows + 31) / 32;
-    const int err = waves <= 2 ? launch_lean_t<D, 2, false, DELTA>(a, row0) : launch_lean_t<D, 4, false, DELTA>(a, row0);
+  const int ns = (a.group + 127) / 128;
+  const int slice = ((a.group + ns - 1) / ns + 31) / 32 * 32;
+  for (int row0 = 0; row0 < a.group; row0 += slice) {
+    const int waves = slice / 32;
+    const int err = waves <= 2 ? launch_lean_t<D, 2, false, DELTA>(a, row0)
+                  : waves == 3 ? launch_lean_t<D, 3, false, DELTA>(a, row0) : launch_lean_t<D, 4, false, DELTA>(a, row0);
     if (err) return err;
   }
   return 0;

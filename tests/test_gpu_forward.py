@@ -52,6 +52,9 @@ RANDOM_CASES = [
     (64, 64, 300, 500, 1.0), (128, 128, 333, 700, 1.0), (128, 48, 200, 300, 2.0), (128, 16, 70, 129, 1.0),
     (128, 192, 500, 900, 1.0), (128, 256, 600, 300, 1.5), (64, 32, 100, 64, 1.0), (128, 80, 250, 1000, 3.0),
     (64, 128, 257, 2000, 1.0), (128, 128, 128, 4100, 8.0),
+    # groups wider than 128 rows run as equal slices: 224 -> 2 x 128 (the last group's 2 rows leave the
+    # second slice empty), 160 -> 2 x 96 (ragged second slice)
+    (128, 224, 450, 800, 1.0), (64, 160, 333, 600, 1.0),
 ]
 
 
