@@ -368,7 +368,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ v8,
     const float* __restrict__ vscale, const uint16_t* __restrict__ vmean, int nbp,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap, int Nq, int Nk, int group, int G,
-    float scale_log2, void* __restrict__ out, float* __restrict__ lse, uint32_t n_units) {
+    float scale_log2, void* __restrict__ out, float* __restrict__ lse, uint32_t n_units, int row0) {
   using L = F8Layout<D, QK4>;
   constexpr int NKS = (L::KSETS + NW - 1) / NW;
   constexpr int NVS = (L::VSETS + NW - 1) / NW;
@@ -383,10 +383,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hi = lane >> 5;
   const int ql = lane & 31;
-  const int r0 = g * group;
-  const int rows_in_group = min(group, Nq - r0);
+  // this launch covers rows [row0, row0 + 32 NW) of the group (wider groups run as several launches)
+  const int r0 = g * group + row0;
+  const int rows_here = min(min(group - row0, NW * 32), Nq - r0);
+  if (rows_here <= 0) return;   // the partial last group may end before this launch's rows
   const int wrow = wave * 32 + ql;
-  const bool row_valid = wrow < rows_in_group;
+  const bool row_valid = wrow < rows_here;
 
   int c = counts[bh * (uint32_t)G + g];
   c = c < 0 ? 0 : (c > cap ? cap : c);
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
 }
 
 template <int D, int NW, bool QK4>
-static int launch_fp8_t(const Fp8FwdArgs& a) {
+static int launch_fp8_t(const Fp8FwdArgs& a, int row0) {
   const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
   const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
@@ -702,21 +704,27 @@ static int launch_fp8_t(const Fp8FwdArgs& a) {
   if (a.out_f32)
     hipLaunchKernelGGL((attn_fwd_fp8<D, NW, true, QK4>), dim3(n_units), dim3(NW * 64), 0, st, a.q, a.k, a.q_scales,
                        a.k_scales, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap, a.Nq,
-                       a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+                       a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, row0);
   else
     hipLaunchKernelGGL((attn_fwd_fp8<D, NW, false, QK4>), dim3(n_units), dim3(NW * 64), 0, st, a.q, a.k, a.q_scales,
                        a.k_scales, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap, a.Nq,
-                       a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units);
+                       a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, row0);
   return (int)hipGetLastError();
 }
 
+// Groups wider than 128 rows run as equal slices of at most 128 rows, one launch per slice, as in the
+// bf16 forward (a six- or eight-wave workgroup leaves most SIMDs of its CU under-filled).
 template <int D, bool QK4>
 static int launch_fp8_d(const Fp8FwdArgs& a) {
-  const int waves = (a.group + 31) / 32;
-  if (waves <= 2) return launch_fp8_t<D, 2, QK4>(a);
-  if (waves <= 4) return launch_fp8_t<D, 4, QK4>(a);
-  if (waves <= 6) return launch_fp8_t<D, 6, QK4>(a);
-  return launch_fp8_t<D, 8, QK4>(a);
+  const int ns = (a.group + 127) / 128;
+  const int slice = ((a.group + ns - 1) / ns + 31) / 32 * 32;
+  for (int row0 = 0; row0 < a.group; row0 += slice) {
+    const int waves = slice / 32;
+    const int err = waves <= 2 ? launch_fp8_t<D, 2, QK4>(a, row0)
+                  : waves == 3 ? launch_fp8_t<D, 3, QK4>(a, row0) : launch_fp8_t<D, 4, QK4>(a, row0);
+    if (err) return err;
+  }
+  return 0;
 }
 
 int launch_fp8_fwd(const Fp8FwdArgs& a) {
