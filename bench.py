@@ -146,21 +146,21 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
-    import torch
-    import sparse_self_attention_amd as sattn
     from synth import inputs
-
-    if not os.path.exists(sattn.library_path()):
-        from sparse_self_attention_amd import build
-        build.build()
-    dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
     if args.density is not None:
         if w.mode != "topk" or not 0.0 < args.density <= 1.0:
             print("--density needs a top-k workload and a fraction in (0, 1]", file=sys.stderr)
             sys.exit(2)
         w = dataclasses.replace(w, keep=args.density)
+    import numpy as np
+    import torch
+    import sparse_self_attention_amd as sattn
+
+    if not os.path.exists(sattn.library_path()):
+        from sparse_self_attention_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     qb, kb, vb = inputs.generate(w)
     t_gen = time.perf_counter() - t_gen
