@@ -64,3 +64,53 @@ def test_graph_replays_match_eager(sattn):
         torch.cuda.synchronize()
         for a, b, name in zip(got, ref, ("idx", "counts", "out", "lse")):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
+
+
+def test_lowbit_paths_graph_replays_match_eager(sattn):
+    """V-Smooth quantisation + FP8 forward, and MXFP4 quantisation of Q and K + FP4-score forward, captured
+    together into one graph: every replay reproduces the eager results bit for bit."""
+    rng = np.random.default_rng(19)
+    B, H, D, group, Nq, Nk, topk = 1, 2, 128, 128, 700, 5000, 900
+    bits = lambda shape, std: inputs.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+    q = to_device_bf16(bits((B, H, Nq, D), 1.5), DEV)
+    k = to_device_bf16(bits((B, H, Nk, D), 1.0), DEV)
+    v = to_device_bf16(bits((B, H, Nk, D), 1.0), DEV)
+    idx, cnt = sattn.mask(q, k, group, topk=topk)
+    ws = torch.empty(sattn.vsmooth_workspace_bytes(B, H, Nk, D), dtype=torch.uint8, device=DEV)
+
+    def buffers():
+        codes, vscale, vmean = sattn.vsmooth_quantize(v, workspace=ws)
+        q4, qs = sattn.mx4_quantize(q)
+        k4, ks = sattn.mx4_quantize(k)
+        o8, l8 = sattn.fp8_forward(q, k, codes, vscale, vmean, idx, cnt, group)
+        o4, l4 = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, idx, cnt, group)
+        return [codes, vscale, vmean, q4, qs, k4, ks, o8, l8, o4, l4]
+
+    def step(b):
+        codes, vscale, vmean, q4, qs, k4, ks, o8, l8, o4, l4 = b
+        sattn.vsmooth_quantize(v, codes=codes, vscale=vscale, vmean=vmean, workspace=ws)
+        sattn.mx4_quantize(q, codes=q4, scales=qs)
+        sattn.mx4_quantize(k, codes=k4, scales=ks)
+        sattn.fp8_forward(q, k, codes, vscale, vmean, idx, cnt, group, out=o8, lse=l8)
+        sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, idx, cnt, group, out=o4, lse=l4)
+
+    ref = buffers()
+    torch.cuda.synchronize()
+    got = [t.clone() for t in ref]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(got)                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(got)
+    for rep in range(3):
+        for t in got:                   # eager work between the replays
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: buffer {i} differs from the eager run"
