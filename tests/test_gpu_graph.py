@@ -114,3 +114,56 @@ def test_lowbit_paths_graph_replays_match_eager(sattn):
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a, b), f"replay {rep}: buffer {i} differs from the eager run"
+
+
+def test_cached_and_delta_paths_graph_replays_match_eager(sattn):
+    """Dense pass (lse), cached slice mask, Chipmunk column-sum lists and one delta step captured together:
+    with the delta state reset before each replay, every replay reproduces the eager run bit for bit."""
+    rng = np.random.default_rng(23)
+    B, H, D, group, Nq, Nk, topk = 1, 2, 128, 128, 600, 3000, 500
+    bits = lambda shape, std: inputs.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+    q = to_device_bf16(bits((B, H, Nq, D), 1.5), DEV)
+    k = to_device_bf16(bits((B, H, Nk, D), 1.0), DEV)
+    v = to_device_bf16(bits((B, H, Nk, D), 1.0), DEV)
+    G = -(-Nq // group)
+    ws = torch.empty(sattn.mask_workspace_bytes(B, H, Nq, Nk, D, group), dtype=torch.uint8, device=DEV)
+    out_prev = torch.from_numpy(rng.standard_normal((B, H, Nq, D)).astype(np.float32)).to(DEV)
+
+    def buffers():
+        return [torch.empty((B, H, Nq, D), dtype=torch.float32, device=DEV),      # dense out
+                torch.empty((B, H, Nq), dtype=torch.float32, device=DEV),         # lse
+                torch.empty((B, H, G, Nk), dtype=torch.int32, device=DEV),        # cached lists
+                torch.empty((B, H, G), dtype=torch.int32, device=DEV),
+                torch.empty((B, H, G, topk), dtype=torch.int32, device=DEV),      # column-sum lists
+                torch.empty((B, H, G), dtype=torch.int32, device=DEV),
+                torch.zeros((B, H, Nq, D), dtype=torch.float32, device=DEV),      # delta state (fresh)
+                torch.empty((B, H, Nq, D), dtype=torch.float32, device=DEV)]      # delta output
+
+    def step(b):
+        dout, lse, ci, cc, si, sc, fresh, out = b
+        sattn.attn(q, k, v, out=dout, lse=lse)
+        sattn.cached_mask(q, k, lse, group, idx=ci, counts=cc)
+        sattn.colsum_mask(q, k, lse, group, topk, idx=si, counts=sc, workspace=ws)
+        sattn.delta_forward(q, k, v, si, sc, group, lse=lse, out_prev=out_prev, fresh=fresh, out=out)
+
+    ref = buffers()
+    step(ref)
+    torch.cuda.synchronize()
+    got = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(got)                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(got)
+    for rep in range(3):
+        for t in got:                   # eager work between the replays; the delta state back to zero
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: buffer {i} differs from the eager run"
