@@ -119,6 +119,7 @@ def _check_qkv(q, k, v=None):
             raise ValueError(f"{name} must be bfloat16")
         if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H, N, D] tensor")
+    _on(q.device, k=k, v=v)
     B, H, Nq, D = q.shape
     if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
         raise ValueError("q and k disagree on B, H or D")
@@ -127,9 +128,40 @@ def _check_qkv(q, k, v=None):
     return B, H, Nq, k.shape[2], D
 
 
-def _check_lse(lse, B, H, Nq):
+def _check_lse(lse, B, H, Nq, dev=None):
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
+    if dev is not None:
+        _on(dev, lse=lse)
+
+
+def _on(dev, **tensors):
+    """Every tensor given (None skipped) must live on `dev`: a host pointer, or one of another device, would
+    reach the kernels as an address they cannot use."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise ValueError(f"{name} must be a tensor on {dev} (got {t.device})")
+
+
+def _check_lists(idx, counts, B, H, G, dev):
+    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
+        raise ValueError("idx and counts must be contiguous int32")
+    if idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
+        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    _on(dev, idx=idx, counts=counts)
+
+
+def _check_out(out, shape, dev):
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 or fp32 tensor of shape {tuple(shape)}")
+    _on(dev, out=out)
+
+
+def _check_workspace(ws, dev):
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _on(dev, workspace=ws)
+    return ws.numel() * ws.element_size()
 
 
 def mask_workspace_bytes(B: int, H: int, Nq: int, Nk: int, D: int, group: int) -> int:
@@ -154,12 +186,14 @@ def mask(q: torch.Tensor, k: torch.Tensor, group: int, *, topk: Optional[int] = 
         idx = torch.empty((B, H, G, cap), dtype=torch.int32, device=q.device)
     if counts is None:
         counts = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    _check_lists(idx, counts, B, H, G, q.device)
     need = lib.sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q.device)
     st = lib.sattn_mask(_ptr(q), _ptr(k), B, H, Nq, Nk, D, group, mode, int(topk or 0),
                         float(thresh or 0.0), scale, _ptr(idx), _ptr(counts), idx.shape[-1],
-                        _ptr(workspace), workspace.numel(), _stream_ptr(q))
+                        _ptr(workspace), ws_bytes, _stream_ptr(q))
     _check("sattn_mask", st)
     return idx, counts
 
@@ -171,17 +205,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor
     lib = _load()
     B, H, Nq, Nk, D = _check_qkv(q, k, v)
     G = -(-Nq // group)
-    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
-        raise ValueError("idx and counts must be contiguous int32")
-    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
-        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    _check_lists(idx, counts, B, H, G, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
-    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 or fp32 tensor shaped like q")
+    _check_out(out, q.shape, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_lse(lse, B, H, Nq, q.device)
     st = lib.sattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk, D,
                            group, scale, _ptr(out), F32 if out.dtype == torch.float32 else BF16, _ptr(lse),
                            _stream_ptr(q))
@@ -198,8 +230,11 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[f
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    _check_out(out, q.shape, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_lse(lse, B, H, Nq, q.device)
     st = lib.attn_forward(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, D, scale, _ptr(out),
                           F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
     _check("attn_forward", st)
@@ -212,7 +247,7 @@ def cached_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int,
     """Full-attention slice mask from a dense pass's lse (sattn_cached_mask); tau defaults to 0.5 / Nk."""
     lib = _load()
     B, H, Nq, Nk, D = _check_qkv(q, k)
-    _check_lse(lse, B, H, Nq)
+    _check_lse(lse, B, H, Nq, q.device)
     tau = 0.5 / Nk if tau is None else float(tau)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     G = -(-Nq // group)
@@ -222,6 +257,7 @@ def cached_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int,
         idx = torch.empty((B, H, G, cap), dtype=torch.int32, device=q.device)
     if counts is None:
         counts = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    _check_lists(idx, counts, B, H, G, q.device)
     st = lib.sattn_cached_mask(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, D, group, tau, scale, _ptr(idx),
                                _ptr(counts), idx.shape[-1], _stream_ptr(q))
     _check("sattn_cached_mask", st)
@@ -234,7 +270,7 @@ def colsum_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int,
     """Top-k keys per group by column sums of attention probabilities with a given lse (sattn_colsum_mask)."""
     lib = _load()
     B, H, Nq, Nk, D = _check_qkv(q, k)
-    _check_lse(lse, B, H, Nq)
+    _check_lse(lse, B, H, Nq, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     G = -(-Nq // group)
     if cap is None:
@@ -243,11 +279,13 @@ def colsum_mask(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, group: int,
         idx = torch.empty((B, H, G, cap), dtype=torch.int32, device=q.device)
     if counts is None:
         counts = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    _check_lists(idx, counts, B, H, G, q.device)
     need = lib.sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q.device)
     st = lib.sattn_colsum_mask(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, D, group, int(topk), scale, _ptr(idx),
-                               _ptr(counts), idx.shape[-1], _ptr(workspace), workspace.numel(), _stream_ptr(q))
+                               _ptr(counts), idx.shape[-1], _ptr(workspace), ws_bytes, _stream_ptr(q))
     _check("sattn_colsum_mask", st)
     return idx, counts
 
@@ -260,19 +298,16 @@ def delta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     lib = _load()
     B, H, Nq, Nk, D = _check_qkv(q, k, v)
     G = -(-Nq // group)
-    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
-        raise ValueError("idx and counts must be contiguous int32")
-    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
-        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
-    _check_lse(lse, B, H, Nq)
+    _check_lists(idx, counts, B, H, G, q.device)
+    _check_lse(lse, B, H, Nq, q.device)
     for name, t in (("out_prev", out_prev), ("fresh", fresh)):
         if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous fp32 device tensor shaped like q")
+        _on(q.device, **{name: t})
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
-    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 or fp32 tensor shaped like q")
+    _check_out(out, q.shape, q.device)
     st = lib.sattn_delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk,
                                  D, group, scale, _ptr(lse), _ptr(out_prev), _ptr(fresh), _ptr(out),
                                  F32 if out.dtype == torch.float32 else BF16, _stream_ptr(q))
@@ -303,11 +338,13 @@ def vsmooth_quantize(v: torch.Tensor, *, codes: Optional[torch.Tensor] = None, v
             or tuple(vscale.shape) != (B, H, D) or vmean.dtype != torch.bfloat16 or tuple(vmean.shape) != (B, H, D, S)
             or not (codes.is_contiguous() and vscale.is_contiguous() and vmean.is_contiguous())):
         raise ValueError("codes, vscale, vmean: contiguous uint8 [B,H,Nk,D], fp32 [B,H,D], bf16 [B,H,D,S]")
+    _on(v.device, codes=codes, vscale=vscale, vmean=vmean)
     need = lib.sattn_vsmooth_workspace_bytes(B, H, Nk, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+    ws_bytes = _check_workspace(workspace, v.device)
     st = lib.sattn_vsmooth_quantize(_ptr(v), B, H, Nk, D, _ptr(codes), _ptr(vscale), _ptr(vmean), _ptr(workspace),
-                                    workspace.numel(), _stream_ptr(v))
+                                    ws_bytes, _stream_ptr(v))
     _check("sattn_vsmooth_quantize", st)
     return codes, vscale, vmean
 
@@ -321,21 +358,20 @@ def fp8_forward(q: torch.Tensor, k: torch.Tensor, codes: torch.Tensor, vscale: t
     B, H, Nq, Nk, D = _check_qkv(q, k)
     G = -(-Nq // group)
     S = lib.sattn_vsmooth_mean_stride(Nk)
-    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
-        raise ValueError("idx and counts must be contiguous int32")
-    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
-        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    _check_lists(idx, counts, B, H, G, q.device)
     if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, Nk, D) or vscale.dtype != torch.float32
             or tuple(vscale.shape) != (B, H, D) or vmean.dtype != torch.bfloat16 or tuple(vmean.shape) != (B, H, D, S)
             or not (codes.is_contiguous() and vscale.is_contiguous() and vmean.is_contiguous())):
         raise ValueError("codes, vscale, vmean must be what vsmooth_quantize returns for a V shaped like k")
+    _on(q.device, codes=codes, vscale=vscale, vmean=vmean)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
-    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 or fp32 tensor shaped like q")
+    _check_out(out, q.shape, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_lse(lse, B, H, Nq, q.device)
     st = lib.sattn_fp8_forward(_ptr(q), _ptr(k), _ptr(codes), _ptr(vscale), _ptr(vmean), _ptr(idx), _ptr(counts),
                                idx.shape[-1], B, H, Nq, Nk, D, group, scale, _ptr(out),
                                F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
@@ -357,6 +393,7 @@ def mx4_quantize(x: torch.Tensor, *, codes: Optional[torch.Tensor] = None, scale
     if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, N, D // 2) or scales.dtype != torch.uint8
             or tuple(scales.shape) != (B, H, N, 4) or not codes.is_contiguous() or not scales.is_contiguous()):
         raise ValueError("codes must be contiguous uint8 [B,H,N,D/2] and scales uint8 [B,H,N,4]")
+    _on(x.device, codes=codes, scales=scales)
     _check("sattn_mx4_quantize", lib.sattn_mx4_quantize(_ptr(x), B, H, N, D, _ptr(codes), _ptr(scales), _stream_ptr(x)))
     return codes, scales
 
@@ -377,21 +414,20 @@ def fp4_forward(q4: torch.Tensor, q_scales: torch.Tensor, k4: torch.Tensor, k_sc
         raise ValueError("q4 / k4 must be [B,H,N,D/2] and their scales [B,H,N,4] (mx4_quantize)")
     G = -(-Nq // group)
     S = lib.sattn_vsmooth_mean_stride(Nk)
-    if idx.dtype != torch.int32 or counts.dtype != torch.int32 or not idx.is_contiguous() or not counts.is_contiguous():
-        raise ValueError("idx and counts must be contiguous int32")
-    if tuple(idx.shape[:3]) != (B, H, G) or tuple(counts.shape) != (B, H, G):
-        raise ValueError("idx must be [B, H, G, cap] and counts [B, H, G] with G = ceil(Nq / group)")
+    _check_lists(idx, counts, B, H, G, q4.device)
     if (codes.dtype != torch.uint8 or tuple(codes.shape) != (B, H, Nk, D) or vscale.dtype != torch.float32
             or tuple(vscale.shape) != (B, H, D) or vmean.dtype != torch.bfloat16 or tuple(vmean.shape) != (B, H, D, S)
             or not (codes.is_contiguous() and vscale.is_contiguous() and vmean.is_contiguous())):
         raise ValueError("codes, vscale, vmean must be what vsmooth_quantize returns for V")
+    _on(q4.device, k4=k4, q_scales=q_scales, k_scales=k_scales, codes=codes, vscale=vscale, vmean=vmean)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q4.device)
-    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (B, H, Nq, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 or fp32 [B, H, Nq, D] tensor")
+    _check_out(out, (B, H, Nq, D), q4.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q4.device)
+    if lse is not None:
+        _check_lse(lse, B, H, Nq, q4.device)
     st = lib.sattn_fp4_forward(_ptr(q4), _ptr(q_scales), _ptr(k4), _ptr(k_scales), _ptr(codes), _ptr(vscale), _ptr(vmean),
                                _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk, D, group, scale, _ptr(out),
                                F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q4))
@@ -412,11 +448,16 @@ def permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Reorder the tokens of a bf16 [B,H,N,D] device tensor by a device int32 permutation."""
     lib = _load()
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [B, H, N, D] device tensor")
     B, H, N, D = x.shape
     if out is None:
         out = torch.empty_like(x)
-    if perm.dtype != torch.int32 or not perm.is_cuda or perm.numel() != N:
-        raise ValueError("perm must be a device int32 tensor of N entries")
+    if out.dtype != torch.bfloat16 or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like x")
+    if perm.dtype != torch.int32 or perm.numel() != N or not perm.is_contiguous():
+        raise ValueError("perm must be a contiguous device int32 tensor of N entries")
+    _on(x.device, out=out, perm=perm)
     _check("sattn_permute_tokens", lib.sattn_permute_tokens(_ptr(x), _ptr(out), _ptr(perm), B, H, N, D,
                                                             1 if inverse else 0, _stream_ptr(x)))
     return out
