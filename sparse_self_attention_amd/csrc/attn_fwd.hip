@@ -28,7 +28,9 @@
 //    taken from the first block and moved only when a later block's probabilities could exceed
 //    2^64 (checked through the block's partial row sums; an overflow trips the same check), so
 //    the common path has no max reduction and no rescale.  P enters the PV product rounded to
-//    bf16; the row sum adds the fp32 probabilities.
+//    bf16, and the row sum adds those same rounded values, so the output is exactly their weighted
+//    mean of V: with the max taken lazily the dominant probability is not 1, and summing the fp32
+//    values instead would pass its rounding error (up to 2^-8 of it) straight into the output.
 //  * LDS rows are XOR-swizzled in 16-byte chunks: K rows so that 16 consecutive rows read at
 //    the same chunk hit distinct banks, V rows so that the 4-row transposed reads do.
 #include <stdlib.h>
@@ -203,14 +205,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     uint32_t pk[8];
     float lsum;
     auto exps = [&]() {
-      lsum = 0.0f;
+      float ps[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r + 1], scale_log2, -m_run));
-        pk[r >> 1] = pack_bf16x2(p0, p1);
-        lsum += p0 + p1;   // plain fp32 adds: a dot2 row sum would stall on the running MFMAs
+        const uint32_t w = pack_bf16x2(p0, p1);
+        pk[r >> 1] = w;
+        // the rounded pair, unpacked by integer operations (they issue beside the MFMAs; a dot2 sum
+        // of the pairs would stall behind them)
+        ps[r >> 1] = __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
       }
+      lsum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     };
     if (!DELTA && j == 0) take_max();
     exps();
