@@ -11,7 +11,7 @@ from synth import inputs
 # Parity bar on the fp32 output given identical index lists.
 MAX_ABS = 1e-2
 REL_L2 = 5e-3
-# lse = m ln2 + ln(l), where l sums bf16-rounded probabilities (each within 2^-9 relative), so its
+# lse = m ln2 + ln(l), where l sums the bf16-rounded probabilities (each within 2^-9 relative), so its
 # error is bounded by about 2^-9; allow two bf16 half-ulps of slack.
 LSE_ABS = 4e-3
 # mask key sets may differ only on keys whose oracle score is this close (logit scale) to the cut

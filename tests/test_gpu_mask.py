@@ -121,7 +121,7 @@ def test_crowded_cut_bin_uses_global_passes(sattn):
 def test_maximum_key_count(sattn):
     """Nk at the mask's limit (131072 keys: the longest sample row the select's LDS takes, the largest
     bitmaps): top-k and threshold lists of both groups against the oracle, then the forward on the
-    top-k lists against the oracle."""
+    oracle's top-k lists against the oracle."""
     rng = np.random.default_rng(131072)
     D, group, Nq, Nk = 64, 128, 256, 131072
     qb = _bits(rng, (1, 1, Nq, D), 2.0)
@@ -135,10 +135,13 @@ def test_maximum_key_count(sattn):
     ref_t = oracle.mask_ref(f64(qb), f64(kb), group, "thresh", thresh=1e-5)
     idx_t, cnt_t = _gpu_mask(sattn, qb, kb, group, thresh=1e-5)
     check_mask_sets(idx_t, cnt_t, ref_t, units, "max Nk thresh", exact_counts=False)
+    # the forward on the oracle's top-k lists (both sides take the same lists; none comes from the GPU)
     q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
-    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+    ridx = np.ascontiguousarray(np.maximum(ref["idx"], 0).astype(np.int32))
+    rcnt = np.ascontiguousarray(ref["counts"].astype(np.int32))
+    ti, tc = torch.from_numpy(ridx).to(DEV), torch.from_numpy(rcnt).to(DEV)
     out, lse = sattn.forward(q, k, v, ti, tc, group, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    ro, rl = oracle.sparse_attention_ref(f64(qb), f64(kb), f64(vb), idx, cnt, group, scale_of(D))
+    ro, rl = oracle.sparse_attention_ref(f64(qb), f64(kb), f64(vb), ridx, rcnt, group, scale_of(D))
     check_out(out.cpu().numpy(), ro, "max Nk forward")
     check_lse(lse.cpu().numpy(), rl, "max Nk forward")
