@@ -1,15 +1,21 @@
 """A seeded sweep over the shapes the entry points accept: head dim 64 or 128, any group size that is a
-multiple of 16 up to 256, query and key counts drawn log-uniformly (single tokens, ragged tails, many
-tiles), top-k or threshold masks.  For each shape the GPU mask is checked against the fp64 oracle's sets,
-and the GPU sparse forward, fed the oracle's own lists, against the oracle's output and lse."""
+multiple of 16 up to 256, query and key counts drawn log-uniformly (single tokens, ragged tails) or
+uniformly over several groups and tiles, queries of standard deviation 1, 2 or 4 (peaked rows).
+Each path against the fp64 oracle, on inputs the oracle made or seeded lists, never on a GPU result:
+the mask (sets) and the sparse forward on the oracle's lists; the dense path; the cached slice mask and
+the column-sum lists with the oracle's lse; the sparse-delta step; the FP8 value path on the oracle's
+quantisation."""
 import os
 
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import check_lse, check_mask_sets, check_out, f64, scale_of, to_device_bf16
+from gpu_util import (MASK_BAND, check_lse, check_mask_sets, check_out, check_out_scaled, f64, scale_of,
+                      structured_lists, to_device_bf16, vsmooth_to_device)
 from synth import inputs
+from test_gpu_cached import check_cached_sets
+from test_gpu_delta import LOG_BAND, _check_colsum_sets
 
 pytestmark = pytest.mark.gpu
 
@@ -17,18 +23,22 @@ torch = pytest.importorskip("torch")
 DEV = "cuda:0"
 
 
+def _shape(rng, i, n, nq_max=800, nk_max=9000):
+    D = int(rng.choice([64, 128]))
+    group = 16 * int(rng.integers(1, 17))
+    if i < n // 3:       # small and single-token shapes
+        Nq = int(np.exp(rng.uniform(0.0, np.log(nq_max))))
+        Nk = int(np.exp(rng.uniform(0.0, np.log(nk_max))))
+    else:                # several groups and key tiles with ragged ends
+        Nq, Nk = int(rng.integers(nq_max // 4, nq_max + 1)), int(rng.integers(300, nk_max + 1))
+    return D, group, max(Nq, 1), max(Nk, 1)
+
+
 def _draw_cases(n, seed=2024):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
-        D = int(rng.choice([64, 128]))
-        group = 16 * int(rng.integers(1, 17))
-        if i < n // 3:       # small and single-token shapes
-            Nq = int(np.exp(rng.uniform(0.0, np.log(800.0))))
-            Nk = int(np.exp(rng.uniform(0.0, np.log(9000.0))))
-        else:                # several groups and key tiles with ragged ends
-            Nq, Nk = int(rng.integers(200, 801)), int(rng.integers(300, 9001))
-        Nq, Nk = max(Nq, 1), max(Nk, 1)
+        D, group, Nq, Nk = _shape(rng, i, n)
         if rng.random() < 0.6:
             mode, param = "topk", int(rng.integers(1, Nk + 1))
         else:
@@ -49,8 +59,33 @@ def sattn():
     return s
 
 
-def _bits(rng, shape, std=1.0):
-    return inputs.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+def _bits(rng, shape, std=1.0, offset=None):
+    x = rng.standard_normal(shape) * std
+    if offset is not None:
+        x = x + offset
+    return inputs.f32_to_bf16_bits(x.astype(np.float32))
+
+
+def _draw_list(rng, n, extra):
+    out = []
+    for i in range(n):
+        D, group, Nq, Nk = _shape(rng, i, n)
+        out.append((i, D, group, Nq, Nk) + extra(rng, D, group, Nq, Nk))
+    return out
+
+
+def _ids(cases):
+    return [f"{c[0]}-D{c[1]}-M{c[2]}-{c[3]}x{c[4]}" for c in cases]
+
+
+STD = lambda rng: float(rng.choice([1.0, 2.0, 4.0]))
+DENSE_CASES = _draw_list(np.random.default_rng(7001), 9, lambda rng, D, g, nq, nk: (STD(rng),))
+CACHED_CASES = _draw_list(np.random.default_rng(7002), 9, lambda rng, D, g, nq, nk: (
+    float(10.0 ** rng.uniform(-5.0, -1.0)) if rng.random() < 0.5 else 0.5 / nk, STD(rng)))
+COLSUM_CASES = _draw_list(np.random.default_rng(7003), 9, lambda rng, D, g, nq, nk: (
+    int(rng.integers(1, nk + 1)), int(rng.integers(1, nk + 1)), STD(rng)))
+FP8_CASES = _draw_list(np.random.default_rng(7004), 9, lambda rng, D, g, nq, nk: (
+    int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-D{c[1]}-M{c[2]}-{c[3]}x{c[4]}-{c[5]}" for c in CASES])
@@ -78,3 +113,92 @@ def test_mask_then_forward(sattn, case):
     ro, rl = oracle.sparse_attention_ref(f64(qb), f64(kb), f64(vb), ridx, rcnt, group, scale_of(D))
     check_out(out.cpu().numpy(), ro, f"sweep {i} forward")
     check_lse(lse.cpu().numpy(), rl, f"sweep {i} forward")
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=_ids(DENSE_CASES))
+def test_dense(sattn, case):
+    i, D, _, Nq, Nk, q_std = case
+    print(f"dense sweep case {case}", flush=True)
+    rng = np.random.default_rng(2000 + i)
+    qb = _bits(rng, (1, 2, Nq, D), q_std)
+    kb, vb = _bits(rng, (1, 2, Nk, D)), _bits(rng, (1, 2, Nk, D))
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    out, lse = sattn.attn(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.dense_attention_ref(f64(qb), f64(kb), f64(vb), scale_of(D))
+    check_out(out.cpu().numpy(), ro, f"dense sweep {i}")
+    check_lse(lse.cpu().numpy(), rl, f"dense sweep {i}")
+
+
+@pytest.mark.parametrize("case", CACHED_CASES, ids=_ids(CACHED_CASES))
+def test_cached_mask(sattn, case):
+    i, D, group, Nq, Nk, tau, q_std = case
+    print(f"cached sweep case {case}", flush=True)
+    rng = np.random.default_rng(3000 + i)
+    qb, kb = _bits(rng, (1, 2, Nq, D), q_std), _bits(rng, (1, 2, Nk, D))
+    q64, k64 = f64(qb), f64(kb)
+    lse = oracle.row_lse_ref(q64, k64, scale_of(D))
+    q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
+    idx, cnt = sattn.cached_mask(q, k, torch.from_numpy(lse.astype(np.float32)).to(DEV), group, tau=tau)
+    torch.cuda.synchronize()
+    ref = oracle.cached_mask_ref(q64, k64, group, tau, scale_of(D))
+    G = -(-Nq // group)
+    rows = {(0, h, g): ref["m"][0, h, g] for h in range(2) for g in range(G)}
+    check_cached_sets(idx.cpu().numpy(), cnt.cpu().numpy(), rows, ref["log_tau"], MASK_BAND + 1e-5,
+                      f"cached sweep {i}")
+
+
+@pytest.mark.parametrize("case", COLSUM_CASES, ids=_ids(COLSUM_CASES))
+def test_colsum_and_delta(sattn, case):
+    i, D, group, Nq, Nk, topk, cap, q_std = case
+    print(f"colsum/delta sweep case {case}", flush=True)
+    rng = np.random.default_rng(4000 + i)
+    B, H = 1, 2
+    G = -(-Nq // group)
+    qb = _bits(rng, (B, H, Nq, D), q_std)
+    kb, vb = _bits(rng, (B, H, Nk, D)), _bits(rng, (B, H, Nk, D))
+    q64, k64, v64 = f64(qb), f64(kb), f64(vb)
+    scale = scale_of(D)
+    lse = oracle.row_lse_ref(q64, k64, scale)
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    idx, cnt = sattn.colsum_mask(q, k, t(lse.astype(np.float32)), group, topk)
+    torch.cuda.synchronize()
+    rows = oracle.colsum_scores_ref(q64, k64, group, scale, lse)
+    _check_colsum_sets(idx.cpu().numpy(), cnt.cpu().numpy(), rows, topk, LOG_BAND, f"colsum sweep {i}")
+    # one delta step over seeded lists (not the GPU's) with the oracle's lse
+    counts = rng.integers(0, cap + 1, size=(B, H, G)).astype(np.int32)
+    lists = inputs.random_index_lists(rng, B, H, G, Nk, counts, cap)
+    out_prev = rng.standard_normal((B, H, Nq, D)).astype(np.float32)
+    fresh_prev = (rng.standard_normal((B, H, Nq, D)) * 0.1).astype(np.float32)
+    ref_out, ref_fresh = oracle.delta_forward_ref(q64, k64, v64, lists, counts, group, scale, lse, out_prev, fresh_prev)
+    fresh = t(fresh_prev)
+    out = sattn.delta_forward(q, k, v, t(lists), t(counts), group, lse=t(lse.astype(np.float32)),
+                              out_prev=t(out_prev), fresh=fresh, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_out_scaled(fresh.cpu().numpy(), ref_fresh, f"delta sweep {i} fresh")
+    check_out_scaled(out.cpu().numpy(), ref_out, f"delta sweep {i} out")
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=_ids(FP8_CASES))
+def test_fp8_forward(sattn, case):
+    i, D, group, Nq, Nk, cmax, q_std = case
+    print(f"fp8 sweep case {case}", flush=True)
+    rng = np.random.default_rng(5000 + i)
+    B, H = 1, 2
+    G = -(-Nq // group)
+    qb = _bits(rng, (B, H, Nq, D), q_std)
+    kb = _bits(rng, (B, H, Nk, D))
+    off = np.repeat(rng.uniform(-2, 2, size=(H, -(-Nk // 128), 1)), 128, axis=1)[:, :Nk][None]
+    vb = _bits(rng, (B, H, Nk, D), 1.0, off)
+    counts = rng.integers(1, cmax + 1, size=(B, H, G)).astype(np.int32)
+    idx = structured_lists(rng, B, H, G, Nk, counts, "random")
+    rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
+    ro, rl = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale_of(D))
+    codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
+    q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
+    out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, torch.from_numpy(idx).to(DEV),
+                                 torch.from_numpy(counts).to(DEV), group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_out(out.cpu().numpy(), ro, f"fp8 sweep {i}")
+    check_lse(lse.cpu().numpy(), rl, f"fp8 sweep {i}")
