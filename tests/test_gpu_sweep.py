@@ -3,8 +3,8 @@ multiple of 16 up to 256, query and key counts drawn log-uniformly (single token
 uniformly over several groups and tiles, queries of standard deviation 1, 2 or 4 (peaked rows).
 Each path against the fp64 oracle, on inputs the oracle made or seeded lists, never on a GPU result:
 the mask (sets) and the sparse forward on the oracle's lists; the dense path; the cached slice mask and
-the column-sum lists with the oracle's lse; the sparse-delta step; the FP8 value path on the oracle's
-quantisation."""
+the column-sum lists with the oracle's lse; the sparse-delta step; the FP8 value path and the 4-bit
+score path on the oracle's quantisation."""
 import os
 
 import numpy as np
@@ -16,6 +16,7 @@ from gpu_util import (MASK_BAND, check_lse, check_mask_sets, check_out, check_ou
 from synth import inputs
 from test_gpu_cached import check_cached_sets
 from test_gpu_delta import LOG_BAND, _check_colsum_sets
+from test_gpu_fp4 import _run as run_fp4
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +86,8 @@ CACHED_CASES = _draw_list(np.random.default_rng(7002), 9, lambda rng, D, g, nq, 
 COLSUM_CASES = _draw_list(np.random.default_rng(7003), 9, lambda rng, D, g, nq, nk: (
     int(rng.integers(1, nk + 1)), int(rng.integers(1, nk + 1)), STD(rng)))
 FP8_CASES = _draw_list(np.random.default_rng(7004), 9, lambda rng, D, g, nq, nk: (
+    int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
+FP4_CASES = _draw_list(np.random.default_rng(7005), 9, lambda rng, D, g, nq, nk: (
     int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
 
 
@@ -202,3 +205,10 @@ def test_fp8_forward(sattn, case):
     torch.cuda.synchronize()
     check_out(out.cpu().numpy(), ro, f"fp8 sweep {i}")
     check_lse(lse.cpu().numpy(), rl, f"fp8 sweep {i}")
+
+
+@pytest.mark.parametrize("case", FP4_CASES, ids=_ids(FP4_CASES))
+def test_fp4_forward(sattn, case):
+    i, D, group, Nq, Nk, cmax, q_std = case
+    print(f"fp4 sweep case {case}", flush=True)
+    run_fp4(sattn, np.random.default_rng(6000 + i), D, group, Nq, Nk, cmax, "random", q_std=q_std)
