@@ -24,6 +24,8 @@
 //                 scan and mbcnt.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/sattn.h"
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -740,19 +742,19 @@ static int launch_mask_d(const MaskArgs& a) {
   const int kchunks = (a.Nk + SC_KT * 32 - 1) / (SC_KT * 32);
   const float log_tau = a.mode == 1 ? (a.thresh > 0.0f ? logf(a.thresh) : -INFINITY) : 0.0f;
   // dynamic LDS of the select kernel can exceed 64 KB (86 KB at the largest Nk); the limit is raised once
-  // per device (setting it again is harmless, so concurrent first calls need no lock)
+  // per device (setting it again is harmless, so concurrent first calls need no lock, only atomic flags)
   constexpr int MAX_DEVICES = 64;
-  static bool lds_attr_set[MAX_DEVICES] = {};
+  static std::atomic<bool> lds_attr_set[MAX_DEVICES];   // static storage: zero-initialised (false)
   int dev = 0;
   err = (int)hipGetDevice(&dev);
   if (err) return err;
-  if (dev < 0 || dev >= MAX_DEVICES || !lds_attr_set[dev]) {
+  if (dev < 0 || dev >= MAX_DEVICES || !lds_attr_set[dev].load(std::memory_order_relaxed)) {
     const int max_lds = (int)select_lds_bytes(SATTN_MASK_MAX_NK, true);
     err = (int)hipFuncSetAttribute((const void*)k_select<true>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (!err)
       err = (int)hipFuncSetAttribute((const void*)k_select<false>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (err) return err;
-    if (dev >= 0 && dev < MAX_DEVICES) lds_attr_set[dev] = true;
+    if (dev >= 0 && dev < MAX_DEVICES) lds_attr_set[dev].store(true, std::memory_order_relaxed);
   }
   for (int bh0 = 0; bh0 < BH; bh0 += hp) {
     const int n = BH - bh0 < hp ? BH - bh0 : hp;
