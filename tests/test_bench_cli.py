@@ -1,5 +1,5 @@
-"""bench.py's command line contract on the host: more than one GPU is refused with a message, before
-any device work."""
+"""bench.py on the host: its command line contract (more than one GPU is refused with a message, before
+any device work; workload arguments are validated) and the CPU oracle-baseline leg."""
 import os
 import subprocess
 import sys
@@ -20,3 +20,21 @@ def test_density_needs_a_fraction_and_a_topk_workload():
                            capture_output=True, text=True, timeout=300, cwd=ROOT)
         assert r.returncode == 2, (extra, r.stderr[-300:])
         assert "--density needs" in r.stderr
+
+
+def test_cpu_baseline_leg_on_the_host():
+    """The oracle-timing leg on a tiny workload with the oracle's own lists: a positive kept-FLOP rate, the
+    sample described, and the partial tail group always in it (units given only their listed rows)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import bench
+    import oracle
+    from synth import inputs
+    w = inputs.WORKLOADS["tiny"]
+    qb, kb, vb = inputs.generate(w)
+    f = lambda b: inputs.bf16_bits_to_f32(b).astype(np.float64)
+    ref = oracle.mask_ref(f(qb), f(kb), w.group, "topk", topk=w.topk)
+    idx = np.maximum(ref["idx"], 0).astype(np.int32)
+    rec = bench.cpu_baseline(w, qb, kb, vb, idx, ref["counts"].astype(np.int32), 3)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s" and rec["value"] > 0.0
+    assert rec["cores"] >= 1 and rec["sample"].startswith("3 (head, group) units")
