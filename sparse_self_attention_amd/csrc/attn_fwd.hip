@@ -25,12 +25,15 @@
 //    accumulators also have one query per lane and the rescale by exp(m_old - m_new) is a
 //    per-lane multiply.
 //  * The softmax runs in base 2 with log2(e) folded into the score scale.  The running max is
-//    taken from the first block and moved only when a later block's probabilities could exceed
-//    2^64 (checked through the block's partial row sums; an overflow trips the same check), so
-//    the common path has no max reduction and no rescale.  P enters the PV product rounded to
-//    bf16, and the row sum adds those same rounded values, so the output is exactly their weighted
-//    mean of V: with the max taken lazily the dominant probability is not 1, and summing the fp32
-//    values instead would pass its rounding error (up to 2^-8 of it) straight into the output.
+//    taken from the first block and moved only when a later block has a probability above 2^64
+//    (or an overflow), checked on the packed bf16 probabilities with integer maxima, so the common
+//    path has no max reduction and no rescale.  P enters the PV product rounded to bf16, and the row
+//    sum adds those same rounded values, so the output is exactly their weighted mean of V: with the
+//    max taken lazily the dominant probability is not 1, and summing the fp32 values instead would
+//    pass its rounding error (up to 2^-8 of it) straight into the output.
+//  * The row sums run on the matrix cores: a 16x16x32 product of the probability registers with a
+//    0/1 selector per block, which takes the ~30 fp32 VALU operations of an adder tree off the SIMDs
+//    that also issue the exponentials.
 //  * LDS rows are XOR-swizzled in 16-byte chunks: K rows so that 16 consecutive rows read at
 //    the same chunk hit distinct banks, V rows so that the 4-row transposed reads do.
 #include <stdlib.h>
@@ -42,10 +45,9 @@
 
 namespace sattn {
 
-// The running max is kept until a probability could reach 2^RESCALE_LOG2 (checked through the block's
-// partial row sums); fp32 and bf16 carry such values exactly, so only the first block and the rare
-// blocks that trip the check take a block max.
-constexpr float RESCALE_LOG2 = 64.0f;
+// The running max is kept until a probability passes 2^64: the bf16 bit pattern of 2^64 (positive
+// bf16 values order like their bit patterns).
+constexpr uint32_t RESCALE_BF16_BITS = 0x5F80u;
 
 template <int D, int BKEYS>
 struct FwdLayout {
@@ -54,7 +56,6 @@ struct FwdLayout {
   static constexpr int ROWS_PER_LOAD = 1024 / RB;     // rows filled by one 64-lane 16-byte load
   static constexpr int ROWSETS = BKEYS / ROWS_PER_LOAD;  // load instructions per K (or V) block
   static constexpr int MAT_BYTES = BKEYS * RB;
-  static constexpr int STAGE_BYTES = 2 * MAT_BYTES;   // K block + V block
   static constexpr int KSTEPS = D / 16;               // MFMA k-steps over the head dim
   static constexpr int DBLK = D / 32;                 // 32-wide output column blocks
   static constexpr int ROWDIV = 16 / NC;              // rows sharing one 256-byte bank sweep
@@ -82,7 +83,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     float* __restrict__ fresh, int row0) {
   using L = FwdLayout<D, BKL>;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_BYTES];
+  // The two stages' K and V tiles are separate LDS objects, so the compiler can tell that the reads of
+  // one stage do not depend on the gather in flight into the other one (no wait for it).
+  __shared__ __attribute__((aligned(1024))) char sk0[L::MAT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv0[L::MAT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[L::MAT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv1[L::MAT_BYTES];
 
   const uint32_t unit = xcd_striped(blockIdx.x, n_units, 128);
   const int g = (int)(unit % (uint32_t)G);
@@ -145,17 +151,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
       const int rs = wave + j * NW;
       const int p = blk * BKL + rs * L::ROWS_PER_LOAD + row_in;
       if (DENSE) keys[j] = p < Nk ? p : Nk - 1;
-      else if (L::ROWSETS % NW == 0 || rs < L::ROWSETS) keys[j] = ilist[p < c ? p : c - 1];
+      else if (L::ROWSETS % NW == 0 || rs < L::ROWSETS)
+        keys[j] = ilist[p < c ? p : c - 1];
     }
   };
-  auto issue = [&](char* stage) {
+  auto issue = [&](char* kst, char* vst) {
 #pragma unroll
     for (int j = 0; j < NRS; ++j) {
       const int rs = wave + j * NW;
       if (L::ROWSETS % NW == 0 || rs < L::ROWSETS) {
-        const uint32_t base = (uint32_t)keys[j] * L::RB;
-        buffer_load_lds_x4(rk, stage + rs * L::ROWS_PER_LOAD * L::RB, base + kch[j]);
-        buffer_load_lds_x4(rv, stage + L::MAT_BYTES + rs * L::ROWS_PER_LOAD * L::RB, base + vch[j]);
+        // an index outside [0, Nk) reads the zero row past the end of the buffer
+        const uint32_t base = min((uint32_t)keys[j], (uint32_t)Nk) * L::RB;
+        buffer_load_lds_x4(rk, kst + rs * L::ROWS_PER_LOAD * L::RB, base + kch[j]);
+        buffer_load_lds_x4(rv, vst + rs * L::ROWS_PER_LOAD * L::RB, base + vch[j]);
       }
     }
   };
@@ -163,19 +171,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   f32x16 o[L::DBLK];
 #pragma unroll
   for (int i = 0; i < L::DBLK; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;
   if (DELTA) m_run = row_valid ? lse_in[(size_t)bh * Nq + r0 + wrow] * 1.4426950408889634f : 0.0f;
+  // Row sums: v_mfma_f32_16x16x32_bf16 with A = the lane's 8 packed probabilities (row l % 16, k-group
+  // l / 16) and B = this selector (column l % 16, k-group l / 16), which is one in column 0 for the even
+  // k-groups (lanes l % 16 and 32 + l % 16, both query l % 16) and in column 1 for the odd ones (query
+  // 16 + l % 16).  Lanes 16 g and 16 g + 1 then hold the sums of queries 4 g + i and 16 + 4 g + i in
+  // lacc[i].  l_carry holds what was moved out of lacc when the running max moved (rare).
+  const uint32_t selw = ((lane & 15) == ((lane >> 4) & 1)) ? 0x3F803F80u : 0u;
+  const bf16x8 sel = __builtin_bit_cast(bf16x8, u32x4{selw, selw, selw, selw});
+  f32x4 lacc = {};
+  float l_carry = 0.0f;
+  auto row_sum = [&]() {   // lacc's sum of this lane's query
+    const int src = 16 * ((ql & 15) >> 2) + (ql >> 4);
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float li = lacc[i];   // (a bit cast of the vector element itself would read element 0)
+      const float x = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(li)));
+      if ((ql & 3) == i) t = x;
+    }
+    return t;
+  };
 
   auto block = [&](auto st, int j) {
     constexpr int ST = decltype(st)::value;
     wait_vmcnt0();
     __syncthreads();
     if (j + 1 < nblk) {
-      issue(smem + (1 - ST) * L::STAGE_BYTES);
+      if (ST == 0) issue(sk1, sv1);
+      else issue(sk0, sv0);
       if (j + 2 < nblk) fetch_keys(j + 2);
     }
-    const char* sk = smem + ST * L::STAGE_BYTES;
-    const char* sv = sk + L::MAT_BYTES;
+    const char* sk = ST == 0 ? sk0 : sk1;
+    const char* sv = ST == 0 ? sv0 : sv1;
     f32x16 sacc = {};
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks) {
@@ -188,8 +217,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + 4 * hi + (r & 3) >= valid) sacc[r] = -INFINITY;
     }
-    // running max: taken on the first block; afterwards only when this block's probabilities could
-    // exceed 2^RESCALE_LOG2 (some lane's partial sum trips the bound, which an exp overflow also does)
+    // running max: taken on the first block; afterwards only when one of this block's probabilities
+    // passes 2^64 (an exp overflow or a NaN does too)
     auto take_max = [&]() {
       float bmax = sacc[0];
 #pragma unroll
@@ -198,36 +227,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
       const float mnew = fmaxf(m_run, bmax);
       const float alpha = (mnew == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
-      l_run *= alpha;
+      l_carry *= alpha;
 #pragma unroll
       for (int i = 0; i < L::DBLK; ++i) o[i] *= alpha;
     };
     uint32_t pk[8];
-    float lsum;
     auto exps = [&]() {
-      float ps[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r + 1], scale_log2, -m_run));
-        const uint32_t w = pack_bf16x2(p0, p1);
-        pk[r >> 1] = w;
-        // the rounded pair, unpacked by integer operations (they issue beside the MFMAs; a dot2 sum
-        // of the pairs would stall behind them)
-        ps[r >> 1] = __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
+        pk[r >> 1] = pack_bf16x2(p0, p1);
       }
-      lsum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     };
     if (!DELTA && j == 0) take_max();
     exps();
-    if (!DELTA && __builtin_amdgcn_ballot_w64(!(lsum <= 0x1p64f)) != 0) {   // also true for inf / nan
-      take_max();
-      exps();
+    if (!DELTA) {
+      // largest probability of the lane, as bf16 bits, by packed 16-bit integer maxima
+      u16x2 mx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mx[i] = __builtin_elementwise_max(__builtin_bit_cast(u16x2, pk[2 * i]), __builtin_bit_cast(u16x2, pk[2 * i + 1]));
+      const u16x2 m2 = __builtin_elementwise_max(__builtin_elementwise_max(mx[0], mx[1]),
+                                                 __builtin_elementwise_max(mx[2], mx[3]));
+      const uint32_t top = m2[0] > m2[1] ? m2[0] : m2[1];
+      if (__builtin_amdgcn_ballot_w64(top > RESCALE_BF16_BITS) != 0) {
+        l_carry += row_sum();
+        lacc = f32x4{};
+        take_max();
+        exps();
+      }
     }
-    l_run += lsum;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const u32x4 bw = {pk[4 * tt], pk[4 * tt + 1], pk[4 * tt + 2], pk[4 * tt + 3]};
+      if (!DELTA) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw), sel, lacc, 0, 0, 0);
 #pragma unroll
       for (int db = 0; db < L::DBLK; ++db) {
         const char* p0 = sv + (tt * 16) * L::RB + voff[db];
@@ -244,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 
   if (nblk > 0) {
     fetch_keys(0);
-    issue(smem);
+    issue(sk0, sv0);
     if (nblk > 1) fetch_keys(1);
   }
   int j = 0;
@@ -273,7 +307,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     }
     return;
   }
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = l_carry + row_sum();
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_valid) {
     const size_t orow = ((size_t)bh * Nq + r0 + wrow) * D;

@@ -15,6 +15,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 #define SATTN_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
