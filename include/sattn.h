@@ -218,9 +218,12 @@ int sattn_vsmooth_quantize(const void* v, int B, int H, int Nk, int D, uint8_t* 
  *
  * For query row i of group g with listed keys J (list order, blocks of 64): s = scale q_i.k_j in
  * log2 units; the row's reference point m (a multiple of 1/8) is ceil8 of the first block's max
- * and moves to ceil8(block max) only when a block's max exceeds m + 3/4 (earlier sums are then
- * scaled by 2^(m_old - m_new)); the probability is the E4M3 byte round-half-even(8 (s - m) + 120)
- * clamped to [0, 126] (the summary's 8 log2 v + 56 with the probability scaled by 2^8);
+ * and moves only when a later block's max exceeds m + 13/16 (a byte would pass 126), then by the
+ * smallest whole number of log2 units that brings that max to or below m (earlier sums are scaled
+ * by the exact power of two 2^(m_old - m_new)); the probability is the E4M3 byte
+ * round-half-even(8 (s - m) + 120) clamped to [0, 126] (the summary's 8 log2 v + 56 with the
+ * probability scaled by 2^8).  While every byte is a normal code this equals ExpCast in one pass at
+ * the final m: the result does not depend on the block size or on where the moves fall;
  *     out[i] = sum_j p_j (vscale * E4M3(codes[j]) + mean_block(j)) / sum_j p_j,
  *     lse[i] = ln(sum_j p_j) + (m - 8) ln 2.
  *   q, k, idx, counts, cap, group, scale, out, out_dtype, lse: as sattn_forward (same list

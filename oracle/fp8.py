@@ -11,22 +11,25 @@ V-Smart/ExpCast summary (itinai.com), its second and third paragraphs:
   * ExpCast-FP8: an E4M3 byte is close to 8 log2(v) + 56, so the probability byte is one
     multiply-add of the log-domain score plus a constant, with no exponential and no cast.
 
-Readings where the summary is silent (each is what the GPU path computes as well):
+Readings where the summary is silent:
   * block mean: the exact mean of the block's tokens (the last block may be shorter),
     rounded to bf16 (nearest, ties to even); the residual r = v - mean in fp32;
   * channel scale: the power of two s = 2^e with the smallest e such that 448 s >= max |r|
     over all tokens of the head (s = 1 when the residual is 0), so r / s is exact and
     lands in [-448, 448]; codes = E4M3(r / s), nearest with ties to even;
-  * probabilities: the online softmax runs over blocks of 64 listed keys in list order
-    (LongLive DiT blog, "Online Softmax").  The reference point m of a row lies on the 1/8
-    grid of log2 units so that 8 x + bias is one multiply-add of the raw score plus an
-    integer: m = ceil8(block max) on the first block; a later block moves it only when one
-    of its bytes would pass 126, the largest finite code (block max > m + 13/16), and then
-    by the smallest whole number of log2 units that brings the block max to or below it,
-    so the weights gathered so far are scaled by an exact power of two.  The byte is
-    round-half-even(8 (x - m) + 120), set to 0 below 0: the bias 56 with the probability
-    scaled by 2^8, so the row's largest weight sits near 256 and only weights below 2^-14
-    of it fall into the subnormal codes;
+  * probabilities: ExpCast inside the online softmax (LongLive DiT blog, "Online Softmax"),
+    which runs over blocks of 64 listed keys in list order.  For the byte to be one
+    multiply-add of the raw score plus an integer, the subtracted reference point m of a row
+    must lie on the 1/8 grid of log2 units; for the sums gathered before a move to be rescaled
+    exactly, a move must be by whole log2 units (then a byte before the move, scaled, is the
+    byte after it).  The one free choice left is the grid phase, taken from the first block:
+    m = ceil8(block max); a later block moves it only when one of its bytes would pass 126,
+    the largest finite code (block max > m + 13/16), and then by the smallest whole number of
+    log2 units that brings the block max to or below it.  While every byte is a normal code
+    the result is therefore the one-pass ExpCast at that phase, whatever the block size and
+    wherever the moves fall.  The byte is round-half-even(8 (x - m) + 120), set to 0 below 0:
+    the bias 56 with the probability scaled by 2^8, so the row's largest weight sits near 256
+    and only weights below 2^-14 of it fall into the subnormal codes;
   * the row sum adds the decoded probabilities; out = sum_j p_j (s v8_j + mean_b(j)) / l;
     lse = ln(l 2^(m - 8)).
 Where a decision is integer (a code, a byte), the oracle takes it on the values the

@@ -124,3 +124,101 @@ def structured_lists(rng, B, H, G, Nk, counts, kind):
                     counts[b, h, g] = keys.size
                 idx[b, h, g, :keys.size] = keys
     return idx
+
+
+# ExpCast (V-Smart/ExpCast summary, third paragraph): each probability byte is at most one code from the
+# exactly rounded one, which bounds the per-row total variation of the weights from the exact softmax by
+# 3.64 %.  Over the normal E4M3 range the decoded weight lies within [0.9576, 1.1077] of the exact
+# probability (scaled), whose worst split gives that 3.64 %; the lse of the ExpCast weights is therefore
+# within [ln 0.9576, ln 1.1077] of the exact one.
+EXPCAST_TV = 0.0364
+EXPCAST_LSE = (math.log(0.9576), math.log(1.1077))
+
+
+def check_expcast_bound(o_gpu, l_gpu, o_exact, l_exact, vrange, what, slack=2e-3):
+    """Output of an ExpCast path against the exact restricted softmax over the same (dequantised) values:
+    with weights at total variation TV <= 3.64 % from the exact ones, |out - exact| <= TV * (max - min of
+    the listed value rows) per channel; the lse is within the weight ratio's logarithm.  `vrange` has the
+    per-row channel ranges; the slack covers fp32 accumulation."""
+    o_gpu = o_gpu.astype(np.float64)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
+    err = np.abs(o_gpu - o_exact)
+    bound = EXPCAST_TV * vrange + slack
+    worst = float((err / bound).max())
+    assert worst <= 1.0, f"{what}: |out - exact| reaches {worst:.3f} of the ExpCast bound (max err {err.max():.3g})"
+    fin = np.isfinite(l_exact)
+    d = l_gpu.astype(np.float64)[fin] - l_exact[fin]
+    if d.size:
+        assert EXPCAST_LSE[0] - slack <= d.min() and d.max() <= EXPCAST_LSE[1] + slack, \
+            f"{what}: lse - exact in [{d.min():.4f}, {d.max():.4f}]"
+    return worst
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_vsmooth_head(name: str, h: int):
+    """The oracle's V-Smooth quantisation of one head of a workload's V (codes, scale, mean with a head axis of 1)."""
+    import oracle
+    _, (_, _, vb) = workload(name)
+    return oracle.vsmooth_quantize_ref(f64(vb[:, h:h + 1]))
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_mx4_head(name: str, which: str, h: int):
+    """The oracle's MXFP4 codes and exponents of one head of a workload's Q or K."""
+    import oracle
+    _, (qb, kb, _) = workload(name)
+    x = qb if which == "q" else kb
+    return oracle.mx4_quantize_ref(f64(x[:, h:h + 1]))
+
+
+def value_ranges(vhat, idx, counts, group, n_q):
+    """[B,H,Nq,D]: per row, the per-channel range (max - min) of the value rows its group lists."""
+    B, H, _, D = vhat.shape
+    G = idx.shape[2]
+    r = np.zeros((B, H, n_q, D))
+    for b in range(B):
+        for h in range(H):
+            for g in range(G):
+                c = int(counts[b, h, g])
+                if c:
+                    rows = vhat[b, h, idx[b, h, g, :c]]
+                    r[b, h, g * group:min((g + 1) * group, n_q)] = rows.max(axis=0) - rows.min(axis=0)
+    return r
+
+
+def onehot_case(rng, H, Nq, group, Nk, D=128):
+    """Q, K and per head a set U of D keys whose V rows are the unit vectors e_0 .. e_{D-1}; every group
+    lists a subset of its head's U.  V-Smooth turns V[U[i]] into exactly (1 + 2^-7) e_i (block mean 2^-7,
+    channel scale 2^-8, residual code 256) and every other listed row into 0, so a row's output is its
+    weights times 1 + 2^-7, read in U's order."""
+    G = -(-Nq // group)
+    U = np.stack([np.sort(rng.choice(Nk, size=D, replace=False)) for _ in range(H)])
+    v = np.zeros((1, H, Nk, D))
+    for h in range(H):
+        v[0, h, U[h], np.arange(D)] = 1.0
+    sizes = [D, 100, 65, 64, 17, 1, 33, 128]
+    counts = np.zeros((1, H, G), dtype=np.int32)
+    idx = np.zeros((1, H, G, D), dtype=np.int32)
+    for h in range(H):
+        for g in range(G):
+            c = sizes[(h * G + g) % len(sizes)]
+            counts[0, h, g] = c
+            idx[0, h, g, :c] = np.sort(rng.choice(U[h], size=c, replace=False))
+    return U, inputs.f32_to_bf16_bits(v.astype(np.float32)), idx, counts
+
+
+def onehot_total_variation(out, U, idx, counts, probs, group, Nq):
+    """Per-row total variation between the weights read off the one-hot output and the exact ones."""
+    tvs = []
+    H, G = counts.shape[1], counts.shape[2]
+    for h in range(H):
+        pos = {int(u): i for i, u in enumerate(U[h])}
+        for g in range(G):
+            P = probs(h, g)                                   # exact restricted softmax rows [rows, Nk]
+            r0 = g * group
+            w_exact = np.zeros((P.shape[0], U.shape[1]))
+            for j in idx[0, h, g, :counts[0, h, g]]:
+                w_exact[:, pos[int(j)]] = P[:, j]
+            w_gpu = out[0, h, r0:r0 + P.shape[0]].astype(np.float64) / (1.0 + 2.0 ** -7)
+            tvs.append(0.5 * np.abs(w_gpu - w_exact).sum(axis=1))
+    return np.concatenate(tvs)

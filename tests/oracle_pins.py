@@ -606,7 +606,7 @@ def _fp8_brute_row(s2, vrows, t):
 
 def check_fp8_attention(vsmooth, fp8_attn, decode_table, dequant):
     """The FP8 attention path: per-element loops with the row's reference point on the 1/8 grid (moved
-    only past 3/4), bytes round-half-even(8 (x - m) + 120) and the decoded value rows; equal scores give
+    only when a byte would pass 126, by whole log2 units), bytes round-half-even(8 (x - m) + 120) and the decoded value rows; equal scores give
     the plain mean of the listed value rows and lse = ln c; one key gives its value row; and the
     output and lse stay within the ExpCast error of the exact restricted softmax over the same
     dequantised values (the summary's 3.64 % total-variation bound), with large per-block means."""
@@ -677,6 +677,77 @@ def check_fp8_attention(vsmooth, fp8_attn, decode_table, dequant):
     out1, lse1 = fp8_attn(q, k, codes, vs, vm, idx1, cnt1, M, scale)
     assert np.allclose(out1[0, 0], vhat[0, 0, 200], atol=1e-12)
     assert not out1[0, 1, :M].any() and np.all(np.isneginf(lse1[0, 1, :M]))
+
+
+def _expcast_one_pass(s2, vrows, t, m):
+    """ExpCast weights of one row at a single reference point m (log2 units, no blocks): the byte of key j
+    is 8 (s2_j - m) + 120 rounded half to even and held to [0, 126], its weight the E4M3 value of that
+    byte; out = the weighted mean of the value rows, lse = ln(sum of weights) + (m - 8) ln 2."""
+    y = 8.0 * (np.asarray(s2, dtype=np.float64) - m) + 120.0
+    fl = np.floor(y)
+    up = (y - fl > 0.5) | ((y - fl == 0.5) & (fl % 2 == 1))
+    byte = np.clip(fl + up, 0, 126).astype(np.int64)
+    w = t[byte]
+    l = math.fsum(w)
+    out = np.array([math.fsum(w * vrows[:, d]) for d in range(vrows.shape[1])]) / l
+    return out, math.log(l) + (m - 8.0) * math.log(2.0), byte
+
+
+def check_fp8_reference_point(vsmooth, fp8_attn, decode_table, dequant):
+    """The online reference point of the FP8 path changes nothing it should not.  It sits on the 1/8 grid
+    of log2 units (so that the byte is one multiply-add of the raw score plus an integer) with its phase
+    set by the first block of 64 listed keys, and it moves only by whole log2 units, so a byte computed
+    before a move and scaled by the move's power of two is the byte computed after it, as long as both
+    are normal E4M3 codes.  Hence the blocked online result equals ExpCast in one pass at
+    m = ceil8(max of the first 64 scores) + K, for the smallest whole K >= 0 that keeps every byte at or
+    below 126, and at any larger whole K while every byte stays normal; and with the row's maximum in
+    the first block no point moves, so the block size does not matter."""
+    t = decode_table()
+    rng = np.random.default_rng(61)
+    ln2 = math.log(2.0)
+    n, D = 256, 4
+    cases = []
+    for a in (0.0, 3.3, -7.1):
+        cases.append(a + np.arange(n) * (2.0 / 64) + rng.uniform(-0.3, 0.3, n))     # a move every block
+        cases.append(a + rng.uniform(0.0, 10.0, n))                                # random, max anywhere
+        ramp = a + np.arange(n) * (9.0 / n)
+        cases.append(ramp + rng.uniform(-0.05, 0.05, n) + rng.integers(0, 8, n) / 8.0)  # on and off the 1/8 grid
+    vb = _bf16_values(rng, (1, 1, n, D))
+    vb[0, 0, :128] += 2.0
+    codes, vs, vm = vsmooth(vb)
+    vhat = dequant(codes, vs, vm)[0, 0]
+    idx = np.arange(n, dtype=np.int32).reshape(1, 1, 1, n)
+    cnt = np.full((1, 1, 1), n, np.int32)
+    moved = 0
+    for s2 in cases:
+        # scores enter as q . k with q = e0 and scale 1: s2 (log2 units) = k[:, 0] / ln 2
+        q = np.zeros((1, 1, 1, D))
+        q[0, 0, 0, 0] = 1.0
+        k = np.zeros((1, 1, n, D))
+        k[0, 0, :, 0] = s2 * ln2
+        s2 = k[0, 0, :, 0] / ln2
+        out, lse = fp8_attn(q, k, codes, vs, vm, idx, cnt, 1, 1.0)
+        m0 = math.ceil(8.0 * s2[:64].max()) / 8.0
+        K = max(0, math.ceil(s2.max() - m0 - 13.0 / 16.0))
+        moved += K > 0
+        want, want_lse, byte = _expcast_one_pass(s2, vhat, t, m0 + K)
+        assert byte.max() <= 126 and byte.min() >= 8 + 8 * 2, "case must keep its bytes normal"
+        assert np.all(np.abs(out[0, 0, 0] - want) <= 1e-12 * (1 + np.abs(want))), (out[0, 0, 0], want)
+        assert abs(lse[0, 0, 0] - want_lse) <= 1e-12
+        for extra in (1, 2):      # a larger whole offset of the point gives the same weights up to 2^-extra
+            w2, l2, _ = _expcast_one_pass(s2, vhat, t, m0 + K + extra)
+            assert np.all(np.abs(w2 - want) <= 1e-12 * (1 + np.abs(want))) and abs(l2 - want_lse) <= 1e-12
+        # the row maximum moved into the first block: no point moves, every block size agrees
+        s2b = s2.copy()
+        jmax = int(np.argmax(s2b))
+        s2b[[0, jmax]] = s2b[[jmax, 0]]
+        k[0, 0, :, 0] = s2b * ln2
+        res = [fp8_attn(q, k, codes, vs, vm, idx, cnt, 1, 1.0, block=bs) for bs in (64, 100, n)]
+        want_b, want_lse_b, _ = _expcast_one_pass(s2b, vhat, t, math.ceil(8.0 * s2b.max()) / 8.0)
+        for o_b, l_b in res:
+            assert np.all(np.abs(o_b[0, 0, 0] - want_b) <= 1e-12 * (1 + np.abs(want_b)))
+            assert abs(l_b[0, 0, 0] - want_lse_b) <= 1e-12
+    assert moved >= 6, moved
 
 
 def check_e2m1(decode_table, encode):

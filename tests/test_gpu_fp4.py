@@ -1,13 +1,17 @@
 """GPU parity of the 4-bit QK^T path: MXFP4 quantisation of queries and keys (sattn_mx4_quantize, bit-exact
 against the oracle) and the FP4-score / FP8-value forward (sattn_fp4_forward) against the fp64 oracle fed
-the oracle's own codes and scales."""
+the oracle's own codes and scales; and the forward against the exact restricted softmax over the
+dequantised queries, keys and values, to the ExpCast bound of the V-Smart/ExpCast summary's third
+paragraph (per-row total variation of the weights below 3.64 %)."""
 import os
 
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import check_lse, check_out, f64, scale_of, structured_lists, to_device_bf16, vsmooth_to_device, workload
+from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out, f64, onehot_case, onehot_total_variation,
+                      oracle_mx4_head, oracle_vsmooth_head, scale_of, structured_lists, to_device_bf16, value_ranges,
+                      vsmooth_to_device, workload)
 from synth import inputs
 
 pytestmark = pytest.mark.gpu
@@ -83,6 +87,12 @@ def _run(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0):
     what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
     check_out(out.cpu().numpy(), ro, what)
     check_lse(lse.cpu().numpy(), rl, what)
+    # the exact restricted softmax over the dequantised queries, keys and values, to the ExpCast bound
+    vhat = oracle.dequantize_ref(vc, vs, vm)
+    eo, el = oracle.sparse_attention_ref(oracle.mx4_dequantize_ref(qc, qe), oracle.mx4_dequantize_ref(kc, ke), vhat,
+                                         idx, counts, group, scale)
+    check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
+                        what + " vs exact softmax")
 
 
 FWD_CASES = [
@@ -137,3 +147,76 @@ def test_fp4_full_size_sampled(sattn):
                                           counts[:, :1, g:g + 1], w.group, scale)
         check_out(out_h[:, :1, r], ro, f"long_70200 fp4 g={g}")
         check_lse(lse_h[:, :1, r], rl, f"long_70200 fp4 g={g}")
+
+
+def test_fp4_weights_total_variation(sattn):
+    """The FP4-score path's ExpCast weights read off a one-hot V: per row, the total variation from the exact
+    restricted softmax of the dequantised MXFP4 scores stays below the summary's 3.64 %."""
+    rng = np.random.default_rng(4364)
+    H, Nq, group, Nk, D = 4, 256, 128, 1024, 128
+    U, vb, idx, counts = onehot_case(rng, H, Nq, group, Nk, D)
+    qb = np.concatenate([inputs.f32_to_bf16_bits((rng.standard_normal((1, 1, Nq, D)) * sd).astype(np.float32))
+                         for sd in (1.0, 2.5, 4.0, 6.0)], axis=1)
+    kb = inputs.f32_to_bf16_bits(rng.standard_normal((1, H, Nk, D)).astype(np.float32))
+    qc, qe = oracle.mx4_quantize_ref(f64(qb))
+    kc, ke = oracle.mx4_quantize_ref(f64(kb))
+    vc, vs, vm = oracle.vsmooth_quantize_ref(f64(vb))
+    q4, qs = (torch.from_numpy(a).to(DEV) for a in _pack(qc, qe))
+    k4, ks = (torch.from_numpy(a).to(DEV) for a in _pack(kc, ke))
+    codes, vscale, vmean = vsmooth_to_device(vc, vs, vm, Nk)
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    out, _ = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qh, kh = oracle.mx4_dequantize_ref(qc, qe), oracle.mx4_dequantize_ref(kc, ke)
+    probs = lambda h, g: oracle.sparse_attention_probs_ref(qh, kh, idx, counts, group, scale_of(D), 0, h, g)[0]
+    tv = onehot_total_variation(out.cpu().numpy(), U, idx, counts, probs, group, Nq)
+    print(f"FP4-score ExpCast weights: per-row total variation mean {tv.mean():.4f}, max {tv.max():.4f}")
+    assert tv.max() <= EXPCAST_TV + 1e-4, f"total variation {tv.max():.4f} above the 3.64 % bound"
+
+
+def test_fp4_full_size_exact_softmax(sattn):
+    """The long-video workload: pooled top-20 % lists from the GPU mask on all 24 heads (fed to both sides),
+    the oracle's MXFP4 keys and V-Smooth values for heads 0 and 23 and its MXFP4 queries for the sampled
+    groups; those groups against the exact restricted softmax of the dequantised inputs."""
+    w, (qb, kb, vb) = workload("long_70200")
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    idx, counts = sattn.mask(q, k, w.group, topk=w.topk)
+    q4, qs = sattn.mx4_quantize(q)
+    k4, ks = sattn.mx4_quantize(k)
+    codes, vscale, vmean = sattn.vsmooth_quantize(v)
+    heads, groups = (0, 23), (0, w.groups // 2, w.groups - 1)
+    ref = {}
+    for h in heads:
+        kc, ke = oracle_mx4_head(w.name, "k", h)
+        a, b = _pack(kc, ke)
+        k4[:, h:h + 1].copy_(torch.from_numpy(a).to(DEV))
+        ks[:, h:h + 1].copy_(torch.from_numpy(b).to(DEV))
+        vc, vs, vm = oracle_vsmooth_head(w.name, h)
+        c0, s0, m0 = vsmooth_to_device(vc, vs, vm, w.n_k)
+        codes[:, h:h + 1].copy_(c0)
+        vscale[:, h:h + 1].copy_(s0)
+        vmean[:, h:h + 1].copy_(m0)
+        qrows = {}
+        for g in groups:
+            r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
+            qc, qe = oracle.mx4_quantize_ref(f64(qb[:, h:h + 1, r]))
+            a, b = _pack(qc, qe)
+            q4[:, h:h + 1, r].copy_(torch.from_numpy(a).to(DEV))
+            qs[:, h:h + 1, r].copy_(torch.from_numpy(b).to(DEV))
+            qrows[g] = oracle.mx4_dequantize_ref(qc, qe)
+        ref[h] = (oracle.mx4_dequantize_ref(kc, ke), oracle.dequantize_ref(vc, vs, vm), qrows)
+    out, lse = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, idx, counts, w.group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    idx_h, cnt_h = idx.cpu().numpy(), counts.cpu().numpy()
+    worst = 0.0
+    for h in heads:
+        kh, vhat, qrows = ref[h]
+        for g in groups:
+            r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
+            ui, uc = idx_h[:, h:h + 1, g:g + 1], cnt_h[:, h:h + 1, g:g + 1]
+            eo, el = oracle.sparse_attention_ref(qrows[g], kh, vhat, ui, uc, w.group, scale_of(w.dim))
+            vr = value_ranges(vhat, ui, uc, w.group, r.stop - r.start)
+            worst = max(worst, check_expcast_bound(out_h[:, h:h + 1, r], lse_h[:, h:h + 1, r], eo, el, vr,
+                                                   f"long_70200 fp4 h={h} g={g} vs exact softmax"))
+    print(f"long_70200 FP4-score forward: worst |out - exact| at {worst:.3f} of the ExpCast bound")

@@ -1,6 +1,8 @@
 """GPU parity of the FP8 value path: V-Smooth quantisation (sattn_vsmooth_quantize, bit-exact against
 the oracle) and the ExpCast / E4M3 P.V forward (sattn_fp8_forward) against the fp64 oracle fed the
-oracle's own codes, scales and block means."""
+oracle's own codes, scales and block means; and the forward against the exact restricted softmax over
+the same dequantised values, to the bound of the V-Smart/ExpCast summary's third paragraph (each byte at
+most one code off, per-row total variation of the weights below 3.64 %)."""
 import math
 import os
 
@@ -8,7 +10,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import check_lse, check_out, f64, scale_of, to_device_bf16, workload, vsmooth_to_device, structured_lists
+from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out, f64, onehot_case, onehot_total_variation,
+                      oracle_vsmooth_head, scale_of, structured_lists, to_device_bf16, value_ranges, vsmooth_to_device,
+                      workload)
 from synth import inputs
 
 pytestmark = pytest.mark.gpu
@@ -89,6 +93,11 @@ def _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0, zero_group=Tr
     what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
     check_out(out.cpu().numpy(), ro, what)
     check_lse(lse.cpu().numpy(), rl, what)
+    # the exact restricted softmax over the same dequantised values, to the summary's ExpCast bound
+    vhat = oracle.dequantize_ref(rc, rs, rm)
+    eo, el = oracle.sparse_attention_ref(f64(qb), f64(kb), vhat, idx, counts, group, scale)
+    check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
+                        what + " vs exact softmax")
     if zero_group and G > 1:
         r = slice((G - 1) * group, Nq)
         assert not out[0, 1, r].any().item() and torch.isneginf(lse[0, 1, r]).all().item()
@@ -119,6 +128,67 @@ def test_fp8_forward_large_logits(sattn):
     """Scores spread over tens of log2 units: the reference point moves, bytes clamp at 0."""
     rng = np.random.default_rng(5)
     _run_case(sattn, rng, 128, 128, 256, 4000, 900, "random", q_std=6.0)
+
+
+def test_fp8_weights_total_variation(sattn):
+    """The GPU's ExpCast weights read directly off a one-hot V: per row, the total variation from the exact
+    restricted softmax stays below the summary's 3.64 % (peaked and flat rows, moves of the reference
+    point with q std 6, lists of 1 to 128 keys)."""
+    rng = np.random.default_rng(364)
+    H, Nq, group, Nk, D = 4, 256, 128, 1024, 128
+    U, vb, idx, counts = onehot_case(rng, H, Nq, group, Nk, D)
+    qb = np.concatenate([_bits(rng, (1, 1, Nq, D), sd) for sd in (1.0, 2.5, 4.0, 6.0)], axis=1)
+    kb = _bits(rng, (1, H, Nk, D))
+    rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
+    vhat = oracle.dequantize_ref(rc, rs, rm)
+    for h in range(H):
+        assert np.array_equal(vhat[0, h, U[h]], (1.0 + 2.0 ** -7) * np.eye(D)), "one-hot V must dequantise exactly"
+    codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
+    q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
+    ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    out, _ = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    scale = scale_of(D)
+    probs = lambda h, g: oracle.sparse_attention_probs_ref(f64(qb), f64(kb), idx, counts, group, scale, 0, h, g)[0]
+    tv = onehot_total_variation(out.cpu().numpy(), U, idx, counts, probs, group, Nq)
+    print(f"ExpCast weights: per-row total variation mean {tv.mean():.4f}, max {tv.max():.4f} ({tv.size} rows)")
+    assert tv.max() <= EXPCAST_TV + 1e-4, f"total variation {tv.max():.4f} above the 3.64 % bound"
+
+
+def test_fp8_full_size_exact_softmax(sattn):
+    """The long-video workload in the benchmark's launch configuration: pooled top-20 % lists from the GPU
+    mask on all 24 heads (fed to both sides), the oracle's V-Smooth codes for heads 0, 11 and 23; sampled
+    groups of those heads against the exact restricted softmax over the dequantised values."""
+    w, (qb, kb, vb) = workload("long_70200")
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    idx, counts = sattn.mask(q, k, w.group, topk=w.topk)
+    codes, vscale, vmean = sattn.vsmooth_quantize(v)
+    heads = (0, 11, 23)
+    quant = {}
+    for h in heads:
+        rc, rs, rm = oracle_vsmooth_head(w.name, h)
+        quant[h] = (rc, rs, rm)
+        c0, s0, m0 = vsmooth_to_device(rc, rs, rm, w.n_k)
+        codes[:, h:h + 1].copy_(c0)
+        vscale[:, h:h + 1].copy_(s0)
+        vmean[:, h:h + 1].copy_(m0)
+    out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, idx, counts, w.group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    idx_h, cnt_h = idx.cpu().numpy(), counts.cpu().numpy()
+    scale = scale_of(w.dim)
+    worst = 0.0
+    for h in heads:
+        vhat = oracle.dequantize_ref(*quant[h])
+        for g in (0, w.groups // 2, w.groups - 1):
+            r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
+            ui, uc = idx_h[:, h:h + 1, g:g + 1], cnt_h[:, h:h + 1, g:g + 1]
+            eo, el = oracle.sparse_attention_ref(f64(qb[:, h:h + 1, r]), f64(kb[:, h:h + 1]), vhat, ui, uc, w.group,
+                                                 scale)
+            vr = value_ranges(vhat, ui, uc, w.group, r.stop - r.start)
+            worst = max(worst, check_expcast_bound(out_h[:, h:h + 1, r], lse_h[:, h:h + 1, r], eo, el, vr,
+                                                   f"long_70200 fp8 h={h} g={g} vs exact softmax"))
+    print(f"long_70200 FP8 forward: worst |out - exact| at {worst:.3f} of the ExpCast bound")
 
 
 def test_fp8_full_size_sampled(sattn):

@@ -18,3 +18,8 @@ def test_vsmooth():
 def test_fp8_attention():
     pins.check_fp8_attention(oracle.vsmooth_quantize_ref, oracle.fp8_attention_ref, oracle.e4m3_decode_table,
                              oracle.dequantize_ref)
+
+
+def test_fp8_reference_point():
+    pins.check_fp8_reference_point(oracle.vsmooth_quantize_ref, oracle.fp8_attention_ref, oracle.e4m3_decode_table,
+                                   oracle.dequantize_ref)

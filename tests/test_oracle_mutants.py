@@ -130,8 +130,24 @@ def test_fp8_mutant_is_caught(name, old, new):
               lambda: pins.check_expcast(m.expcast_byte, m.e4m3_decode_table),
               lambda: pins.check_vsmooth(m.vsmooth_quantize_ref, m.e4m3_decode_table),
               lambda: pins.check_fp8_attention(m.vsmooth_quantize_ref, m.fp8_attention_ref, m.e4m3_decode_table,
-                                               m.dequantize_ref)]
+                                               m.dequantize_ref),
+              lambda: pins.check_fp8_reference_point(m.vsmooth_quantize_ref, m.fp8_attention_ref, m.e4m3_decode_table,
+                                                     m.dequantize_ref)]
     assert _caught(checks), f"no pin catches the planted mistake: {name}"
+
+
+REFERENCE_POINT_MUTANTS = ["reference point off the 1/8 grid", "reference point kept past saturation",
+                           "reference point moved by a fraction", "earlier blocks not rescaled"]
+
+
+@pytest.mark.parametrize("name", REFERENCE_POINT_MUTANTS)
+def test_reference_point_mutant_fails_the_one_pass_pin(name):
+    """The reference-point rule is pinned by a check that does not restate the blocked loop: each of these
+    mutants fails the one-pass ExpCast equivalence on its own."""
+    old, new = next((o, n) for (nm, o, n) in FP8_MUTANTS if nm == name)
+    m = _mutant("oracle.fp8", old, new)
+    assert _caught([lambda: pins.check_fp8_reference_point(m.vsmooth_quantize_ref, m.fp8_attention_ref,
+                                                           m.e4m3_decode_table, m.dequantize_ref)]), name
 
 
 FP4_MUTANTS = [
