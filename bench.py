@@ -7,9 +7,12 @@ by 5 % noise per step) plus the sparse forward over the kept keys.
 
 Prints one JSON line.  `value` is kept-FLOP throughput of the whole job (mask time included);
 the line also carries the forward-only and dense-equivalent rates, the dense control path, the
-roofline of the dominant kernel and the fp64 CPU oracle timed on a bounded sample.
+roofline of the dominant kernel and the fp64 CPU oracle timed on a bounded sample.  Between timed
+steps a 512 MiB scratch write flushes the last-level cache (its time is not counted).  Threshold-mode
+workloads (the chunked window) take their tau from tests/golden/thresholds.json, which an oracle-only
+script writes.
 
-    python bench.py [--steps K] [--warmup W] [--workload long_70200] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload long_70200] [--density f] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -28,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "sparse attn TFLOP/s (kept + dense-equiv) and % MFMA peak at 20% density, 1 GPU"
 PEAK_BF16_TFLOPS = 256 * 4 * 1024 * 2.4e9 / 1e12      # 2516.6: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz
 HBM_PEAK_GBPS = 8000.0
+HOST_CORES_PER_GPU = 16       # host CPU share of one GPU on an MI355X node (8 GPUs, 128 cores)
 MASK_EVERY = 4
 DRIFT = 0.05
 
@@ -41,6 +45,8 @@ def parse():
     p.add_argument("--density", type=float, default=None,
                    help="top-k fraction of the keys kept per group instead of the workload's own (a sweep point)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush-mib", type=int, default=512,
+                   help="scratch write between timed steps that flushes the last-level cache (0: none)")
     p.add_argument("--cpu-units", type=int, default=0, help="oracle units to time (default: 16 per core)")
     p.add_argument("--kernel-only", action="store_true",
                    help="only the timed steps (for profiler runs): no dense path, no CPU baseline")
@@ -76,6 +82,13 @@ def recorded_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def threshold_of(workload: str) -> float:
+    """The pooling threshold of a threshold-mode workload, as calibrated on the oracle by
+    tests/golden/make_thresholds.py."""
+    with open(os.path.join(ROOT, "tests", "golden", "thresholds.json")) as fh:
+        return float(json.load(fh)[workload]["tau"])
+
+
 def kept_flops(counts, w) -> float:
     """4 D sum_{b,h,g} |g| c_g: QK^T and PV multiply-adds over the kept (query, key) pairs."""
     import numpy as np
@@ -89,7 +102,8 @@ def cpu_baseline(w, qb, kb, vb, idx_h, cnt_h, n_units):
     """Time the fp64 oracle on a seeded sample of (head, group) units in one process per core."""
     import multiprocessing as mp
     import numpy as np
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    available = len(os.sched_getaffinity(0))
+    cores = min(available, HOST_CORES_PER_GPU)
     if n_units <= 0:
         n_units = 16 * cores
     rng = np.random.default_rng(1234)
@@ -113,9 +127,10 @@ def cpu_baseline(w, qb, kb, vb, idx_h, cnt_h, n_units):
         dt = time.perf_counter() - t0
     sizes = [min((g + 1) * w.group, w.n_q) - g * w.group for _, g in units]
     flops = sum(4.0 * w.dim * s * len(j[3]) for s, j in zip(sizes, jobs))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(units)} (head, group) units of the step-0 mask, fp64 masked-dense oracle, "
-                      f"one process per core, {dt:.1f} s wall"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "cores_available": available,
+            "kind": "oracle",
+            "sample": f"{len(units)} (head, group) units of the step-0 lists, the fp64 oracle's restricted softmax "
+                      f"over each unit's listed K/V rows, one process per core, {dt:.1f} s wall"}
 
 
 def _slice_bitmap(idx, counts, n_k):
@@ -180,63 +195,89 @@ def main():
         gen.manual_seed(1000 * 3 + s)
         qs.append((qs[-1].float() + DRIFT * rq * torch.randn(q0.shape, device=dev, generator=gen)).to(torch.bfloat16))
         ks.append((ks[-1].float() + DRIFT * rk * torch.randn(k0.shape, device=dev, generator=gen)).to(torch.bfloat16))
+    if w.mode == "thresh":
+        tau = threshold_of(w.name)
+        cap = w.n_k
+        mask_kw = {"thresh": tau}
+    else:
+        tau = None
+        mask_kw = {"topk": w.topk}
     idx = torch.empty((1, w.heads, G, cap), dtype=torch.int32, device=dev)
-    counts = torch.empty((1, w.heads, G), dtype=torch.int32, device=dev)
     ws = torch.empty(sattn.mask_workspace_bytes(1, w.heads, w.n_q, w.n_k, w.dim, w.group), dtype=torch.uint8,
                      device=dev)
     out = torch.empty_like(q0)
     lse = torch.empty((1, w.heads, w.n_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(max(args.flush_mib, 0) << 20, dtype=torch.uint8, device=dev)
+    # one counts buffer per mask call, so that every step's kept FLOPs are known afterwards
+    n_mask_calls = (warm + MASK_EVERY - 1) // MASK_EVERY + (steps + MASK_EVERY - 1) // MASK_EVERY + 1
+    counts_of = [torch.empty((1, w.heads, G), dtype=torch.int32, device=dev) for _ in range(n_mask_calls)]
+    step_counts = []          # counts buffer each timed step's forward used
 
-    def run_steps(n, offset, ev=None):
+    def run_steps(n, offset, ev=None, call0=0):
+        call = call0
         for s in range(n):
             i = offset + s
+            if ev is not None and flush.numel():
+                # last-level cache flush between timed steps, bracketed so its time can be taken out
+                ev["x0"][s].record(stream)
+                flush.zero_()
+                ev["x1"][s].record(stream)
             if s % MASK_EVERY == 0:
+                counts = counts_of[call]
+                call += 1
                 if ev is not None:
                     ev["m0"][s // MASK_EVERY].record(stream)
-                sattn.mask(qs[i], ks[i], w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
+                sattn.mask(qs[i], ks[i], w.group, idx=idx, counts=counts, workspace=ws, **mask_kw)
                 if ev is not None:
                     ev["m1"][s // MASK_EVERY].record(stream)
             if ev is not None:
                 ev["f0"][s].record(stream)
+                step_counts.append(counts)
             sattn.forward(qs[i], ks[i], v, idx, counts, w.group, out=out, lse=lse)
             if ev is not None:
                 ev["f1"][s].record(stream)
+        return call
 
-    run_steps(warm, 0)
+    calls = run_steps(warm, 0)
     torch.cuda.synchronize()
     nm = (steps + MASK_EVERY - 1) // MASK_EVERY
     E = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ev = {"m0": E(nm), "m1": E(nm), "f0": E(steps), "f1": E(steps)}
+    ev = {"m0": E(nm), "m1": E(nm), "f0": E(steps), "f1": E(steps), "x0": E(steps), "x1": E(steps)}
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    run_steps(steps, warm, ev)
+    run_steps(steps, warm, ev, calls)
     t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    flush_ms = sum(a.elapsed_time(b) for a, b in zip(ev["x0"], ev["x1"])) if flush.numel() else 0.0
+    total_ms = t0.elapsed_time(t1) - flush_ms
     fwd_ms = [a.elapsed_time(b) for a, b in zip(ev["f0"], ev["f1"])]
     mask_ms = [a.elapsed_time(b) for a, b in zip(ev["m0"], ev["m1"])]
+    step_flops = [kept_flops(c.cpu().numpy(), w) for c in step_counts]
+    counts = step_counts[0]
     cnt_h = counts.cpu().numpy()
-    kflops = kept_flops(cnt_h, w)
+    kflops = float(np.mean(step_flops))                     # kept FLOPs of one forward launch (mean over steps)
     dflops = 4.0 * w.dim * w.heads * w.n_q * w.n_k * w.batch
     fwd_avg = float(np.mean(fwd_ms))
-    value = kflops * steps / (total_ms * 1e-3) / 1e12
-    fwd_tflops = kflops / (fwd_avg * 1e-3) / 1e12
+    value = sum(step_flops) / (total_ms * 1e-3) / 1e12
+    fwd_tflops = sum(step_flops) / (sum(fwd_ms) * 1e-3) / 1e12
+    kept_pairs = float(np.mean([c.cpu().numpy().astype(np.float64).sum() for c in step_counts]))
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(total_ms / steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.n_q, "head_dim": w.dim,
-                   "group": w.group, "topk": w.topk, "density": round(float(cnt_h.sum()) / (cnt_h.size * w.n_k), 4),
-                   "mask_every": MASK_EVERY, "grid": list(w.grid_k)},
+                   "group": w.group, "mode": w.mode, "topk": w.topk if w.mode == "topk" else None, "tau": tau,
+                   "density": round(kept_pairs / (cnt_h.size * w.n_k), 4), "mask_every": MASK_EVERY,
+                   "grid": list(w.grid_k), "mall_flush_mib": args.flush_mib},
         "kept_tflops_fwd": round(fwd_tflops, 2),
         "dense_equiv_tflops_fwd": round(dflops / (fwd_avg * 1e-3) / 1e12, 2),
         "pct_mfma_peak_kept_fwd": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "pct_mfma_peak_kept_job": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": {"mean": round(fwd_avg, 3), "min": round(min(fwd_ms), 3), "max": round(max(fwd_ms), 3)},
         "mask_ms": {"mean": round(float(np.mean(mask_ms)), 3), "n": len(mask_ms)},
-        "gathered_GBps_fwd": round(float(cnt_h.sum()) * 2 * w.dim * 2 / (fwd_avg * 1e-3) / 1e9, 1),
+        "gathered_GBps_fwd": round(kept_pairs * 2 * w.dim * 2 / (fwd_avg * 1e-3) / 1e9, 1),
     }
     # dominant kernel: the sparse forward (one launch per step)
     traffic = recorded_traffic(w.name)
@@ -267,6 +308,25 @@ def main():
         rec["dense_tflops"] = round(dflops / (dense_ms * 1e-3) / 1e12, 2)
         rec["speedup_vs_dense_fwd"] = round(dense_ms / fwd_avg, 3)
         rec["speedup_vs_dense_job"] = round(dense_ms / (total_ms / steps), 3)
+        # the reused mask against a fresh one on the drifted inputs of the next steps: recall of the slices a
+        # fresh mask keeps (the FG-Attn review asks for the mask's recall; the mask is reused for 4 steps)
+        sidx, scnt = torch.empty_like(idx), torch.empty_like(counts)
+        fidx, fcnt = torch.empty_like(idx), torch.empty_like(counts)
+        sattn.mask(qs[warm], ks[warm], w.group, idx=sidx, counts=scnt, workspace=ws, **mask_kw)
+        recall = []
+        for d in range(1, MASK_EVERY):
+            if warm + d >= total:
+                break
+            sattn.mask(qs[warm + d], ks[warm + d], w.group, idx=fidx, counts=fcnt, workspace=ws, **mask_kw)
+            hit = tot = 0
+            for h in range(w.heads):
+                sm = _slice_bitmap(sidx[0, h], scnt[0, h], w.n_k)
+                fm = _slice_bitmap(fidx[0, h], fcnt[0, h], w.n_k)
+                hit += int((sm & fm).sum())
+                tot += int(fm.sum())
+            recall.append(round(hit / max(tot, 1), 4))
+        rec["stale_mask_recall"] = {"steps_after_mask": list(range(1, len(recall) + 1)), "recall": recall}
+        del sidx, scnt, fidx, fcnt
         # cached slice mask of a dense step (tau = 0.5 / N on the lse that the dense pass returns), and
         # the recall of the step-0 pooled top-k lists against it (the pages' suggested mask check)
         sattn.attn(q0, k0, v, out=out, lse=lse)
@@ -280,7 +340,7 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             cms.append(a.elapsed_time(b))
-        sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
+        sattn.mask(q0, k0, w.group, idx=idx, counts=counts, workspace=ws, **mask_kw)
         torch.cuda.synchronize()
         hit = tot = 0
         for h in range(w.heads):
@@ -290,7 +350,7 @@ def main():
             tot += int(cm.sum())
         rec["cached_mask"] = {"ms": round(float(np.median(cms)), 3), "tau": 0.5 / w.n_k,
                               "density": round(tot / (w.heads * G * w.n_k), 4),
-                              "pooled_topk_recall": round(hit / max(tot, 1), 4)}
+                              "pooled_mask_recall": round(hit / max(tot, 1), 4)}
         del cidx, ccnt
         # Chipmunk sparse deltas on the same step: column-sum top-k lists from the dense lse, then one
         # delta step (stale lse, cached output and fresh part in fp32)
@@ -341,7 +401,7 @@ def main():
         del vws, codes, vscale, vmean, o8, q4, q4s, k4, k4s
     if not args.no_cpu_baseline and not args.kernel_only:
         # oracle on the step-0 inputs with the step-0 lists
-        sattn.mask(q0, k0, w.group, topk=w.topk, idx=idx, counts=counts, workspace=ws)
+        sattn.mask(q0, k0, w.group, idx=idx, counts=counts, workspace=ws, **mask_kw)
         torch.cuda.synchronize()
         rec["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, idx.cpu().numpy(), counts.cpu().numpy(), args.cpu_units)
     rec["input_gen_s"] = round(t_gen, 1)

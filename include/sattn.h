@@ -17,7 +17,15 @@
  *    before any HIP call; on a validation error nothing is launched and no output is touched.
  *    A failed launch returns SATTN_ERR_HIP.  Faults inside a kernel surface at the caller's
  *    next synchronisation.  sattn_last_error() returns a thread-local detail string.
- *  - Thread safety: every entry point may be called from several host threads at once.
+ *  - Thread safety: every entry point may be called from several host threads at once.  In
+ *    validation mode (SATTN_VALIDATE=1) the device check of the index lists is serialised across
+ *    threads (one check word per device); calls that validate wait for each other.
+ *  - Environment: SATTN_VALIDATE=1 checks index lists on the device before sattn_forward,
+ *    sattn_delta_forward, sattn_fp8_forward and sattn_fp4_forward; SATTN_LOG=1 prints one line per
+ *    launch decision (entry point, sizes, kernel variant, workgroups) to stderr; SATTN_SERIAL_GATHER=1
+ *    runs sattn_forward, sattn_delta_forward and attn_forward at pipeline depth 1 (every key block's
+ *    gather completes before the block before it computes), a slower order whose results must equal
+ *    the default double-buffered ones bit for bit (a check for races in the buffering).
  */
 #ifndef SATTN_H
 #define SATTN_H
@@ -278,6 +286,8 @@ int sattn_voxel_permutation(int T, int Hg, int Wg, int vt, int vy, int vx, int32
  * sattn_permute_tokens - dst[b,h,i,:] = src[b,h,perm[i],:] (inverse = 0) or
  * dst[b,h,perm[i],:] = src[b,h,i,:] (inverse = 1) for bf16 [B,H,N,D] tensors; perm is a
  * DEVICE int32 permutation of [0,N).  Applies and undoes the voxel order on the device.
+ * perm is not checked: an entry outside [0,N) leaves its destination row unwritten, and a
+ * repeated entry leaves some destination row unwritten (or, with inverse = 1, written twice).
  */
 int sattn_permute_tokens(const void* src, void* dst, const int32_t* perm, int B, int H, int N, int D,
                          int inverse, void* stream);

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libsattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["attn_fwd.hip", "mask.hip", "cached_mask.hip", "fp8_attn.hip", "util.hip"]
-CXX_SOURCES = ["api.cpp"]
+CXX_SOURCES = ["api.cpp", "mask_sizes.cpp"]
 
 # Packed fp32 VALU forms are kept out of the generated code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -59,12 +59,37 @@ int check_scale(const char* fn, float scale) {
   return SATTN_OK;
 }
 
+bool log_mode() {
+  static const bool on = [] {
+    const char* e = getenv("SATTN_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+bool serial_gather() {
+  const char* e = getenv("SATTN_SERIAL_GATHER");
+  return e != nullptr && e[0] != '\0' && e[0] != '0';
+}
+
 bool validate_mode() {
   const char* e = getenv("SATTN_VALIDATE");
   return e != nullptr && e[0] != '\0' && e[0] != '0';
 }
 
 }  // namespace
+
+namespace sattn {
+void log_launch(const char* fmt, ...) {
+  if (!log_mode()) return;
+  char line[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof(line), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[sattn] %s\n", line);
+}
+}  // namespace sattn
 
 extern "C" {
 
@@ -86,9 +111,10 @@ const char* sattn_last_error(void) { return g_last_error; }
 
 size_t sattn_mask_workspace_bytes(int B, int H, int Nq, int Nk, int D, int group) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (D != 64 && D != 128) || group < 16 || group > MAX_GROUP ||
-      group % 16 != 0 || Nk > SATTN_MASK_MAX_NK)
+      group % 16 != 0 || Nk > SATTN_MASK_MAX_NK || (int64_t)Nq * D * 2 >= I32_MAX || (int64_t)B * H >= I32_MAX)
     return 0;
-  const int G = (Nq + group - 1) / group;
+  const int G = (int)(((int64_t)Nq + group - 1) / group);
+  if ((int64_t)B * H * G >= I32_MAX) return 0;
   return sattn::mask_workspace_bytes(B * H, G, Nk, D);
 }
 
@@ -189,6 +215,7 @@ int sattn_forward(const void* q, const void* k, const void* v, const int32_t* id
   }
   sattn::FwdArgs a{q, k, v, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out, out_dtype == SATTN_F32, lse,
                    false, stream};
+  a.serial = serial_gather();
   const int err = sattn::launch_attn_fwd(a);
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
@@ -222,12 +249,14 @@ int sattn_delta_forward(const void* q, const void* k, const void* v, const int32
   a.lse_in = lse;
   a.out_prev = out_prev;
   a.fresh = fresh;
+  a.serial = serial_gather();
   const int err = sattn::launch_attn_fwd(a);
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
 
 size_t sattn_vsmooth_workspace_bytes(int B, int H, int Nk, int D) {
-  if (B < 1 || H < 1 || Nk < 1 || (D != 64 && D != 128) || (int64_t)B * H >= I32_MAX) return 0;
+  if (B < 1 || H < 1 || Nk < 1 || (D != 64 && D != 128) || (int64_t)B * H >= I32_MAX || (int64_t)Nk * D * 2 >= I32_MAX)
+    return 0;
   return sattn::vsmooth_workspace_bytes(B * H, Nk, D);
 }
 
@@ -332,6 +361,7 @@ int attn_forward(const void* q, const void* k, const void* v, int B, int H, int 
     return fail(SATTN_ERR_ARG, "%s: q, k, v, out must be 16-byte aligned; lse 4-byte aligned", fn);
   sattn::FwdArgs a{q, k, v, nullptr, nullptr, 1, B, H, Nq, Nk, D, 128, scale, out, out_dtype == SATTN_F32, lse,
                    true, stream};
+  a.serial = serial_gather();
   const int err = sattn::launch_attn_fwd(a);
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
@@ -343,6 +373,11 @@ int sattn_voxel_permutation(int T, int Hg, int Wg, int vt, int vy, int vx, int32
     return fail(SATTN_ERR_SHAPE, "%s: grid and voxel sizes must be >= 1", fn);
   const int64_t n = (int64_t)T * Hg * Wg;
   if (n >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: grid too large", fn);
+  // an edge longer than the grid acts as the grid's own extent (t / vt = 0, t % vt = t); clamping keeps the
+  // composite key below T * Hg * Wg
+  vt = std::min(vt, T);
+  vy = std::min(vy, Hg);
+  vx = std::min(vx, Wg);
   const int64_t ny = (Hg + vy - 1) / vy, nx = (Wg + vx - 1) / vx;
   // composite key of (t/vt, y/vy, x/vx, t%vt, y%vy, x%vx): unique per token and order-preserving
   std::vector<std::pair<int64_t, int32_t>> keyed((size_t)n);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap,
     int Nq, int Nk, int group, int G, float scale_log2, void* __restrict__ out, float* __restrict__ lse,
     uint32_t n_units, const float* __restrict__ lse_in, const float* __restrict__ out_prev,
-    float* __restrict__ fresh, int row0) {
+    float* __restrict__ fresh, int row0, int serial) {
   using L = FwdLayout<D, BKL>;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   // The two stages' K and V tiles are separate LDS objects, so the compiler can tell that the reads of
@@ -202,6 +202,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
       if (ST == 0) issue(sk1, sv1);
       else issue(sk0, sv0);
       if (j + 2 < nblk) fetch_keys(j + 2);
+      if (serial) {   // pipeline depth 1: the next block's gather completes before this block computes
+        wait_vmcnt0();
+        __syncthreads();
+      }
     }
     const char* sk = ST == 0 ? sk0 : sk1;
     const char* sv = ST == 0 ? sv0 : sv1;
@@ -332,16 +336,19 @@ static int launch_lean_t(const FwdArgs& a, int row0) {
   const uint32_t n_units = (uint32_t)a.B * (uint32_t)a.H * G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)a.stream;
+  log_launch("attn_fwd_lean<D=%d, waves=%d, %s%s, %s> rows %d.. of each group: %u workgroups x %d threads%s", D, NW,
+             DENSE ? "dense" : "sparse", DELTA ? " delta" : "", a.out_f32 ? "f32" : "bf16", row0, n_units, NW * 64,
+             a.serial ? ", pipeline depth 1" : "");
   if (a.out_f32)
     hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
-                       a.fresh, row0);
+                       a.fresh, row0, a.serial ? 1 : 0);
   else
     hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
-                       a.fresh, row0);
+                       a.fresh, row0, a.serial ? 1 : 0);
   return (int)hipGetLastError();
 }
 

@@ -234,6 +234,8 @@ static int launch_cached_t(const CachedMaskArgs& a) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   const float log2_tau = a.tau > 0.0f ? log2f(a.tau) : -INFINITY;
   const size_t lds = (size_t)((a.Nk + 31) / 32) * 4;   // at most 16 KB (Nk <= 131072)
+  log_launch("k_cached_mask<D=%d, waves=%d>: %u workgroups x %d threads, %zu B of LDS bitmap", D, NW, n_units,
+             NW * 64, lds);
   hipLaunchKernelGGL((k_cached_mask<D, NW, false>), dim3(n_units), dim3(NW * 64), lds, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, a.lse, a.Nq, a.Nk, a.group, (int)G, scale_log2,
                      log2_tau, a.idx, a.counts, a.cap, n_units, nullptr, nullptr, 0);
@@ -258,6 +260,8 @@ static int launch_colsum_t(const ColsumArgs& a) {
   const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
   const uint32_t n_units = (uint32_t)a.nheads * G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
+  log_launch("k_cached_mask<D=%d, waves=%d, column sums> heads %d..%d: %u workgroups x %d threads", D, NW, a.bh0,
+             a.bh0 + a.nheads - 1, n_units, NW * 64);
   hipLaunchKernelGGL((k_cached_mask<D, NW, true>), dim3(n_units), dim3(NW * 64), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, a.lse, a.Nq, a.Nk, a.group, (int)G, scale_log2,
                      0.0f, nullptr, nullptr, 1, n_units, a.scores, a.samples, a.bh0);

@@ -209,6 +209,7 @@ int launch_vsmooth(const VsmoothArgs& a) {
   float* bmax_ws = (float*)((char*)a.workspace + vsmooth_mean_ws_bytes(a.B * a.H, a.Nk, a.D));
   hipStream_t st = (hipStream_t)a.stream;
   const uint16_t* v = (const uint16_t*)a.v;
+  log_launch("k_vs_stats / k_vs_scale / k_vs_codes <D=%d>: %u x %d blocks of 128 tokens", a.D, BH, NB);
   if (a.D == 128) {
     hipLaunchKernelGGL(k_vs_stats<128>, dim3(BH * NB), dim3(256), 0, st, v, a.Nk, NB, mean_ws, bmax_ws);
     hipLaunchKernelGGL(k_vs_scale<128>, dim3(BH), dim3(128 * VS_SLICES), 0, st, bmax_ws, NB, a.vscale);
@@ -277,6 +278,7 @@ int launch_mx4_quant(const Mx4QuantArgs& a) {
   const uint32_t threads = nrows * (uint32_t)(a.D / 32);
   const dim3 grid((threads + 255) / 256);
   hipStream_t st = (hipStream_t)a.stream;
+  log_launch("k_mx4_quant<D=%d>: %u rows, %u workgroups x 256 threads", a.D, nrows, grid.x);
   if (a.D == 128)
     hipLaunchKernelGGL(k_mx4_quant<128>, grid, dim3(256), 0, st, (const uint16_t*)a.x, nrows, a.codes, a.scales);
   else
@@ -701,6 +703,8 @@ static int launch_fp8_t(const Fp8FwdArgs& a, int row0) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   const int nbp = vsmooth_mean_stride(a.Nk);
   hipStream_t st = (hipStream_t)a.stream;
+  log_launch("attn_fwd_fp8<D=%d, waves=%d, %s, %s> rows %d.. of each group: %u workgroups x %d threads", D, NW,
+             QK4 ? "MXFP4 scores" : "bf16 scores", a.out_f32 ? "f32" : "bf16", row0, n_units, NW * 64);
   if (a.out_f32)
     hipLaunchKernelGGL((attn_fwd_fp8<D, NW, true, QK4>), dim3(n_units), dim3(NW * 64), 0, st, a.q, a.k, a.q_scales,
                        a.k_scales, a.codes, a.vscale, (const uint16_t*)a.vmean, nbp, a.idx, a.counts, a.cap, a.Nq,

@@ -27,6 +27,8 @@ struct FwdArgs {
   const float* lse_in = nullptr;
   const float* out_prev = nullptr;
   float* fresh = nullptr;
+  // pipeline depth 1 (SATTN_SERIAL_GATHER=1): each block's gather lands before the previous block computes
+  bool serial = false;
 };
 int launch_attn_fwd(const FwdArgs& a);
 
@@ -88,7 +90,7 @@ int launch_colsum_scores(const ColsumArgs& a);
 // V-Smooth quantisation of V (fp8_attn.hip): E4M3 codes [B,H,Nk,D], power-of-two channel scales
 // [B,H,D] and channel-major scaled block means [B,H,D,vsmooth_mean_stride(Nk)] (bf16 mean / scale).
 constexpr int VSMOOTH_BLOCK = 128;
-inline int vsmooth_blocks(int Nk) { return (Nk + VSMOOTH_BLOCK - 1) / VSMOOTH_BLOCK; }
+inline int vsmooth_blocks(int Nk) { return (int)(((int64_t)Nk + VSMOOTH_BLOCK - 1) / VSMOOTH_BLOCK); }
 inline int vsmooth_mean_stride(int Nk) { return (vsmooth_blocks(Nk) + 3) & ~3; }
 inline size_t vsmooth_mean_ws_bytes(int BH, int Nk, int D) {
   return ((size_t)BH * vsmooth_blocks(Nk) * D * 2 + 255) & ~(size_t)255;
@@ -142,5 +144,8 @@ int launch_permute_tokens(const void* src, void* dst, const int32_t* perm, int B
                           void* stream);
 
 const char* hip_error_string(int e);
+
+// With SATTN_LOG=1 in the environment: one line on stderr per kernel launch (printf format).
+void log_launch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 
 }  // namespace sattn

@@ -33,25 +33,8 @@
 
 namespace sattn {
 
-constexpr size_t SCORE_STAGE_BUDGET = 1024ull << 20;  // bytes of fp32 scores staged per pass
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-
-int mask_heads_per_pass(int BH, int G, int Nk) {
-  const size_t per = (size_t)G * (size_t)score_stride(Nk) * 4;
-  size_t hp = per ? SCORE_STAGE_BUDGET / per : 1;
-  if (hp < 1) hp = 1;
-  if (hp > (size_t)BH) hp = (size_t)BH;
-  return (int)hp;
-}
-
-size_t mask_workspace_bytes(int BH, int G, int Nk, int D) {
-  const size_t means = align256((size_t)BH * G * D * 2);
-  const size_t hp = (size_t)mask_heads_per_pass(BH, G, Nk);
-  const size_t scores = align256(hp * G * score_stride(Nk) * 4);
-  const size_t samples = align256(hp * G * sample_stride(Nk) * 4);
-  return 2 * means + scores + samples;
-}
 
 // ---------------------------------------------------------------------------------------------
 // group mean
@@ -732,6 +715,8 @@ static int launch_mask_d(const MaskArgs& a) {
   const int hp = mask_heads_per_pass(BH, G, a.Nk);
   float* samples = (float*)(ws + 2 * means + align256((size_t)hp * G * score_stride(a.Nk) * 4));
   int err = 0;
+  log_launch("mask<D=%d> mode %s: %d groups per head, %d of %d heads per pass", D,
+             a.mode == 0 ? "top-k" : a.mode == 1 ? "threshold" : "column-sum top-k", G, hp < BH ? hp : BH, BH);
   if (a.mode != 2) {   // the column-sum mode scores from the full queries, not their mean
     hipLaunchKernelGGL((k_group_mean<D>), dim3(BH * G), dim3(256), 0, st, (const uint16_t*)a.q, a.Nq, a.group, G,
                        qhi, qlo);

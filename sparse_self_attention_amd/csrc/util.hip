@@ -1,4 +1,6 @@
 // Token permutation (voxel order) and index-list validation kernels.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -27,6 +29,7 @@ int launch_permute_tokens(const void* src, void* dst, const int32_t* perm, int B
                           void* stream) {
   const size_t total = (size_t)BH * N * (D / 8);
   const size_t blocks = (total + 255) / 256;
+  log_launch("k_permute_tokens%s: %zu workgroups x 256 threads", inverse ? " (inverse)" : "", blocks);
   hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)src, (uint16_t*)dst, perm, N, D, inverse, total);
   return (int)hipGetLastError();
@@ -52,8 +55,13 @@ __global__ __launch_bounds__(256) void k_validate_lists(const int32_t* __restric
   if (bad) atomicOr(&g_validate_flag, bad);
 }
 
+// The flag is one word per device, so validating calls are serialised: each one clears it, launches the
+// check and reads it back before the next one starts (the call synchronises its stream anyway).
+static std::mutex g_validate_mutex;
+
 int validate_index_lists(const int32_t* idx, const int32_t* counts, int cap, int BHG, int Nk, void* stream,
                          int* flag_host) {
+  std::lock_guard<std::mutex> lock(g_validate_mutex);
   hipStream_t st = (hipStream_t)stream;
   static const int zero = 0;
   hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_validate_flag), &zero, sizeof(int), 0,

@@ -38,3 +38,13 @@ def test_cpu_baseline_leg_on_the_host():
     rec = bench.cpu_baseline(w, qb, kb, vb, idx, ref["counts"].astype(np.int32), 3)
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s" and rec["value"] > 0.0
     assert rec["cores"] >= 1 and rec["sample"].startswith("3 (head, group) units")
+
+
+def test_threshold_workload_reads_the_calibrated_tau():
+    """The chunked-window workload's tau comes from the stored oracle calibration (positive, below 1/N_k:
+    a pooled probability threshold that keeps about 30 % of the keys)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from synth import inputs
+    tau = bench.threshold_of("chunked_window")
+    assert 0.0 < tau < 1.0 / inputs.WORKLOADS["chunked_window"].n_k

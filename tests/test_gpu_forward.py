@@ -1,4 +1,5 @@
 """GPU parity of sattn_forward / attn_forward (through the C ABI) against the fp64 oracle."""
+import json
 import os
 
 import numpy as np
@@ -146,6 +147,54 @@ def test_validation_mode_rejects_bad_lists(sattn, monkeypatch):
         assert e.value.status == 7
 
 
+@pytest.mark.parametrize("D,group,Nq,Nk", [(128, 128, 600, 3000), (64, 64, 300, 2000), (128, 192, 500, 4000),
+                                           (128, 48, 200, 700)])
+def test_pipeline_depth_one_equals_two(sattn, monkeypatch, D, group, Nq, Nk):
+    """Race check of the double-buffered gather: with SATTN_SERIAL_GATHER=1 every key block's gather lands
+    before the block before it computes (pipeline depth 1); sparse, dense and delta results must equal the
+    default order bit for bit, over a shape with several waves per group and ragged lists."""
+    rng = np.random.default_rng(D + group + Nq)
+    B, H = 1, 2
+    G = -(-Nq // group)
+    q, k, v = (to_device_bf16(_rand_bits(rng, (B, H, n, D)), DEV) for n in (Nq, Nk, Nk))
+    counts = rng.integers(0, Nk + 1, size=(B, H, G)).astype(np.int32)
+    counts[0, 0, 0] = Nk
+    idx = inputs.random_index_lists(rng, B, H, G, Nk, counts, Nk)
+    it, ct = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
+    lse_in = torch.from_numpy(rng.standard_normal((B, H, Nq)).astype(np.float32) + 6.0).to(DEV)
+    prev = torch.from_numpy(rng.standard_normal((B, H, Nq, D)).astype(np.float32)).to(DEV)
+
+    def run():
+        o, l = sattn.forward(q, k, v, it, ct, group, out_dtype=torch.float32)
+        do, dl = sattn.attn(q, k, v, out_dtype=torch.float32)
+        fresh = torch.zeros_like(prev)
+        xo = sattn.delta_forward(q, k, v, it, ct, group, lse=lse_in, out_prev=prev, fresh=fresh,
+                                 out=torch.empty_like(prev))
+        torch.cuda.synchronize()
+        return [t.cpu() for t in (o, l, do, dl, xo, fresh)]
+
+    monkeypatch.setenv("SATTN_SERIAL_GATHER", "0")
+    two = run()
+    monkeypatch.setenv("SATTN_SERIAL_GATHER", "1")
+    one = run()
+    for name, a, b in zip(("out", "lse", "dense out", "dense lse", "delta out", "delta fresh"), two, one):
+        assert torch.equal(a, b), f"{name}: pipeline depth 1 and 2 differ"
+
+
+def test_log_mode_names_the_kernels(sattn):
+    """SATTN_LOG=1 prints the kernel each launch selects (a child process, so the variable is read fresh)."""
+    import subprocess
+    import sys
+    code = ("import torch, sparse_self_attention_amd as s; q = torch.randn(1, 1, 256, 128, device='cuda')"
+            ".to(torch.bfloat16); i, c = s.mask(q, q, 128, topk=64); s.forward(q, q, q, i, c, 128); "
+            "torch.cuda.synchronize()")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SATTN_LOG="1", PYTHONPATH=root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "[sattn] mask<D=128> mode top-k" in r.stderr and "[sattn] attn_fwd_lean<D=128, waves=4, sparse" in r.stderr
+
+
 def _units(rng, H, G, n):
     us = {(0, 0, 0), (0, H - 1, G - 1)}
     while len(us) < n:
@@ -184,6 +233,10 @@ def test_full_size_sampled(sattn, name):
         p = np.exp(s - s.max(-1, keepdims=True))
         p /= p.sum(-1, keepdims=True)
         tau = float(np.quantile(p, 1.0 - w.keep))
+        # the value the benchmark reads was written by tests/golden/make_thresholds.py with the same rule
+        with open(os.path.join(os.path.dirname(__file__), "golden", "thresholds.json")) as fh:
+            stored = json.load(fh)[name]["tau"]
+        assert abs(stored - tau) <= 1e-12 * tau, (stored, tau)
         ref = {h: oracle.mask_ref(f64(qb[:, h:h + 1]), f64(kb[:, h:h + 1]), w.group, "thresh", thresh=tau)
                for h in mh}
         idx, counts = sattn.mask(q, k, w.group, thresh=tau)
