@@ -90,6 +90,24 @@ int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D
                void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sattn_mask_noalloc - sattn_mask without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid it).
+ *
+ * Same arguments (minus workspace / ws_bytes), modes, outputs and errors as sattn_mask, and the same
+ * kernels, so the key lists equal sattn_mask's bit for bit.  The workspace is a fixed device array of
+ * SATTN_MASK_SCRATCH_BYTES inside the library: every GPU the library runs on holds one until the
+ * process ends, and the call itself allocates nothing.  The heads run in ranges whose workspace fits
+ * that array; a shape for which one head's workspace does not fit (about 4.3 * G * Nk bytes: 549
+ * groups of 70,200 keys need about 164 MB and fit, 1024 groups of 131,072 keys need about 570 MB and
+ * do not) returns SATTN_ERR_UNSUPPORTED before any HIP call.  All calls on one GPU share its array: calls that overlap
+ * on one GPU (other streams or host threads) race and must be serialised by the caller.
+ */
+#define SATTN_MASK_SCRATCH_BYTES (192u << 20)
+int sattn_mask_noalloc(const void* q, const void* k, int B, int H, int Nq, int Nk, int D, int group,
+                       int mode, int topk, float thresh, float scale,
+                       int32_t* idx, int32_t* counts, int cap, void* stream);
+
+/*
  * sattn_colsum_mask - Chipmunk's selection: per group, the topk keys with the largest column sums
  * of attention probabilities.
  *

@@ -25,7 +25,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["mask", "forward", "attn", "cached_mask", "colsum_mask", "delta_forward", "vsmooth_quantize",
+__all__ = ["mask", "mask_noalloc", "forward", "attn", "cached_mask", "colsum_mask", "delta_forward", "vsmooth_quantize",
            "fp8_forward", "mx4_quantize", "fp4_forward", "vsmooth_workspace_bytes", "mask_workspace_bytes", "voxel_permutation", "permute_tokens",
            "library_path", "SattnError", "TOPK", "THRESH"]
 
@@ -61,6 +61,8 @@ def _load():
     lib.sattn_mask_workspace_bytes.restype = Z
     lib.sattn_mask.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, P, P, I, P, Z, P]
     lib.sattn_mask.restype = I
+    lib.sattn_mask_noalloc.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, P, P, I, P]
+    lib.sattn_mask_noalloc.restype = I
     lib.sattn_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, P]
     lib.sattn_forward.restype = I
     lib.attn_forward.argtypes = [P, P, P, I, I, I, I, I, F, P, I, P, P]
@@ -195,6 +197,24 @@ def mask(q: torch.Tensor, k: torch.Tensor, group: int, *, topk: Optional[int] = 
                         float(thresh or 0.0), scale, _ptr(idx), _ptr(counts), idx.shape[-1],
                         _ptr(workspace), ws_bytes, _stream_ptr(q))
     _check("sattn_mask", st)
+    return idx, counts
+
+
+def mask_noalloc(q: torch.Tensor, k: torch.Tensor, group: int, *, topk: Optional[int] = None,
+                 thresh: Optional[float] = None, scale: Optional[float] = None, idx: torch.Tensor,
+                 counts: torch.Tensor):
+    """sattn_mask with the library's fixed device scratch as workspace (sattn_mask_noalloc): the caller
+    passes the outputs and nothing is allocated.  Calls that overlap on one GPU race on the scratch."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k)
+    if (topk is None) == (thresh is None):
+        raise ValueError("pass exactly one of topk= or thresh=")
+    mode = TOPK if topk is not None else THRESH
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check_lists(idx, counts, B, H, -(-Nq // group), q.device)
+    st = lib.sattn_mask_noalloc(_ptr(q), _ptr(k), B, H, Nq, Nk, D, group, mode, int(topk or 0),
+                                float(thresh or 0.0), scale, _ptr(idx), _ptr(counts), idx.shape[-1], _stream_ptr(q))
+    _check("sattn_mask_noalloc", st)
     return idx, counts
 
 

@@ -17,7 +17,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["attn_fwd.hip", "mask.hip", "cached_mask.hip", "fp8_attn.hip", "util.hip"]
+HIP_SOURCES = ["attn_fwd.hip", "mask.hip", "cached_mask.hip", "fp8_attn.hip", "util.hip", "noalloc.hip"]
 CXX_SOURCES = ["api.cpp", "mask_sizes.cpp"]
 
 # Packed fp32 VALU forms are kept out of the generated code.

@@ -118,10 +118,12 @@ size_t sattn_mask_workspace_bytes(int B, int H, int Nq, int Nk, int D, int group
   return sattn::mask_workspace_bytes(B * H, G, Nk, D);
 }
 
-int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D, int group, int mode, int topk,
-               float thresh, float scale, int32_t* idx, int32_t* counts, int cap, void* workspace, size_t ws_bytes,
-               void* stream) {
-  static const char* fn = "sattn_mask";
+}  // extern "C"
+
+namespace {
+// Host checks shared by sattn_mask and sattn_mask_noalloc.
+int check_mask_args(const char* fn, const void* q, const void* k, int B, int H, int Nq, int Nk, int D, int group,
+                    int mode, int topk, float thresh, float scale, const int32_t* idx, const int32_t* counts, int cap) {
   if (!q || !k || !idx || !counts) return fail(SATTN_ERR_NULL, "%s: q, k, idx and counts must be non-NULL", fn);
   if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
   if (int r = check_group(fn, group)) return r;
@@ -138,12 +140,45 @@ int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D
   } else {
     return fail(SATTN_ERR_ARG, "%s: mode = %d is neither SATTN_TOPK nor SATTN_THRESH", fn, mode);
   }
+  if ((int64_t)B * H * ((Nq + group - 1) / group) >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many groups", fn);
+  return SATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sattn_mask(const void* q, const void* k, int B, int H, int Nq, int Nk, int D, int group, int mode, int topk,
+               float thresh, float scale, int32_t* idx, int32_t* counts, int cap, void* workspace, size_t ws_bytes,
+               void* stream) {
+  static const char* fn = "sattn_mask";
+  if (int r = check_mask_args(fn, q, k, B, H, Nq, Nk, D, group, mode, topk, thresh, scale, idx, counts, cap)) return r;
   const size_t need = sattn_mask_workspace_bytes(B, H, Nq, Nk, D, group);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256))
     return fail(SATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-byte aligned), got %zu", fn, need, ws_bytes);
   sattn::MaskArgs a{q, k, B, H, Nq, Nk, D, group, mode, topk, thresh, scale, idx, counts, cap,
                     workspace, ws_bytes, stream};
   const int err = sattn::launch_mask(a);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
+int sattn_mask_noalloc(const void* q, const void* k, int B, int H, int Nq, int Nk, int D, int group, int mode,
+                       int topk, float thresh, float scale, int32_t* idx, int32_t* counts, int cap, void* stream) {
+  static const char* fn = "sattn_mask_noalloc";
+  if (int r = check_mask_args(fn, q, k, B, H, Nq, Nk, D, group, mode, topk, thresh, scale, idx, counts, cap)) return r;
+  const int G = (Nq + group - 1) / group;
+  const size_t one = sattn::mask_workspace_bytes(1, G, Nk, D);
+  if (one > SATTN_MASK_SCRATCH_BYTES)
+    return fail(SATTN_ERR_UNSUPPORTED, "%s: one head needs %zu bytes of workspace, the device scratch holds %u "
+                "(fewer groups or keys, or sattn_mask with a caller's workspace)", fn, one, SATTN_MASK_SCRATCH_BYTES);
+  // the most heads per call whose workspace fits (the size grows with the head count)
+  int lo = 1, hi = B * H;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (sattn::mask_workspace_bytes(mid, G, Nk, D) <= SATTN_MASK_SCRATCH_BYTES) lo = mid;
+    else hi = mid - 1;
+  }
+  sattn::MaskArgs a{q, k, B, H, Nq, Nk, D, group, mode, topk, thresh, scale, idx, counts, cap, nullptr, 0, stream};
+  const int err = sattn::launch_mask_noalloc(a, lo);
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
 

@@ -57,6 +57,9 @@ struct MaskArgs {
 int mask_heads_per_pass(int BH, int G, int Nk);
 size_t mask_workspace_bytes(int BH, int G, int Nk, int D);
 int launch_mask(const MaskArgs& a);
+// sattn_mask_noalloc: launch_mask over ranges of heads_per_call heads with the library's device scratch as
+// the workspace (noalloc.hip).
+int launch_mask_noalloc(const MaskArgs& a, int heads_per_call);
 
 struct CachedMaskArgs {
   const void* q;
