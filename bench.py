@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cpu-units", type=int, default=0, help="oracle units to time (default: 16 per core)")
     p.add_argument("--kernel-only", action="store_true",
                    help="only the timed steps (for profiler runs): no dense path, no CPU baseline")
+    p.add_argument("--mfma-probe-only", action="store_true",
+                   help="only the MFMA rate probe (back-to-back bf16 MFMAs on random data), for its profile")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the steps, run one plain device copy of this many MiB (a known-size kernel "
                         "for scaling FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -133,6 +135,43 @@ def cpu_baseline(w, qb, kb, vb, idx_h, cnt_h, n_units):
                       f"over each unit's listed K/V rows, one process per core, {dt:.1f} s wall"}
 
 
+def mfma_probe(dev, launches=5):
+    """Measured bf16 MFMA rate of this GPU: libsattn_probe.so's back-to-back v_mfma_f32_32x32x16_bf16 on random
+    data, two waves per SIMD on every CU; the median launch, and the shader clock the waves report."""
+    import ctypes
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_self_attention_amd", "libsattn_probe.so"))
+    lib.sattn_probe_mfma_rate.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sattn_probe_mfma_rate.restype = ctypes.c_int
+    workgroups, iters = 2 * 256, 2000
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2516)
+    data = torch.randn(65536 * 2, device=dev, generator=gen).to(torch.bfloat16)      # 256 KiB of random bf16
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    cycles = torch.empty(workgroups * 4, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ms, clk = [], []
+    for _ in range(launches + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        err = lib.sattn_probe_mfma_rate(data.data_ptr(), sink.data_ptr(), cycles.data_ptr(), workgroups, iters,
+                                        stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if err:
+            raise RuntimeError(f"MFMA probe launch failed: {err}")
+        ms.append(a.elapsed_time(b))
+        clk.append(float(cycles.max().item()) / (ms[-1] * 1e-3) / 1e9)
+    ms, clk = ms[1:], clk[1:]                     # the first launch warms up
+    flops = workgroups * 4 * iters * 16 * 32768.0
+    med = float(np.median(ms))
+    tf = flops / (med * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4),
+            "shader_clock_ghz": round(float(np.median(clk)), 3), "ms": round(med, 3),
+            "what": "v_mfma_f32_32x32x16_bf16 back to back on random bf16 operands, 2 waves per SIMD, all CUs"}
+
+
 def _slice_bitmap(idx, counts, n_k):
     """[G, n_k] bool device tensor of the kept (group, key) slices of one head's lists."""
     import torch
@@ -164,6 +203,13 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.mfma_probe_only:
+        import torch
+        if not os.path.exists(os.path.join(ROOT, "sparse_self_attention_amd", "libsattn_probe.so")):
+            from sparse_self_attention_amd import build
+            build.build()
+        print(json.dumps({"mfma_probe": mfma_probe(torch.device("cuda:0"), launches=10)}), flush=True)
+        return
     from synth import inputs
     w = inputs.WORKLOADS[args.workload]
     if args.density is not None:
@@ -294,6 +340,10 @@ def main():
         rec["copy_calibration_bytes"] = src.numel() * 4
         del src, dst
     if not args.kernel_only:
+        # the chip's measured bf16 MFMA rate, and the sparse forward against it
+        probe = mfma_probe(dev)
+        rec["mfma_probe"] = probe
+        rec["roofline"]["frac_of_measured_mfma_rate"] = round(fwd_tflops / probe["tflops"], 4)
         # dense control path on the step-0 inputs
         dmss = []
         for _ in range(3):

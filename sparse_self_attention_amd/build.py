@@ -1,7 +1,8 @@
 """Build libsattn.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
 Usage: python -m sparse_self_attention_amd.build   (or call build()).
-Objects go to sparse_self_attention_amd/_build/, the library to sparse_self_attention_amd/libsattn.so.
+Objects go to sparse_self_attention_amd/_build/, the library to sparse_self_attention_amd/libsattn.so and the
+benchmark's MFMA rate probe to sparse_self_attention_amd/libsattn_probe.so.
 """
 from __future__ import annotations
 
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsattn.so")
+PROBE_LIB = os.path.join(PKG, "libsattn_probe.so")     # the benchmark's MFMA rate probe
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["attn_fwd.hip", "mask.hip", "cached_mask.hip", "fp8_attn.hip", "util.hip", "noalloc.hip"]
@@ -51,6 +53,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, LIB)
+    # the benchmark's MFMA rate probe: a library of its own, outside the attention ABI
+    probe_o = os.path.join(OUT_DIR, "probe_mfma.hip.o")
+    logs.append(_run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "probe_mfma.hip"), "-o", probe_o]))
+    logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", probe_o, "-o", PROBE_LIB + ".tmp"]))
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
         for l in logs:
             if l.strip():

@@ -48,3 +48,13 @@ def test_threshold_workload_reads_the_calibrated_tau():
     from synth import inputs
     tau = bench.threshold_of("chunked_window")
     assert 0.0 < tau < 1.0 / inputs.WORKLOADS["chunked_window"].n_k
+
+
+def test_mfma_probe_library_exports_its_entry_point():
+    """The benchmark's MFMA rate probe is built beside the attention library and loads on the host."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_self_attention_amd", "libsattn_probe.so")
+    if not os.path.exists(path):
+        from sparse_self_attention_amd import build
+        build.build()
+    assert hasattr(ctypes.CDLL(path), "sattn_probe_mfma_rate")
