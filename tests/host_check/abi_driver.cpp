@@ -68,6 +68,12 @@ int main() {
   EXPECT(sattn_mask(P, P, 1, 2, 300, 500, 128, 64, SATTN_TOPK, 10, 0, 0.1f, I, I, 10, nullptr, ws, nullptr), SATTN_ERR_WORKSPACE);
   EXPECT(sattn_mask(P, P, 1, 2, 300, 500, 128, 64, SATTN_TOPK, 10, 0, 0.1f, I, I, 10, P, ws, nullptr), SATTN_ERR_HIP);
   EXPECT(sattn_colsum_mask(P, P, F, 1, 2, 300, 500, 128, 64, 10, 0.1f, I, I, 10, P, ws, nullptr), SATTN_ERR_HIP);
+  EXPECT(sattn_mask_noalloc(P, P, 2, 24, 70200, 70200, 128, 128, SATTN_TOPK, 14040, 0, 0.1f, I, I, 14040, nullptr),
+         SATTN_ERR_HIP);
+  EXPECT(sattn_mask_noalloc(P, P, 1, 1, 131072, 131072, 64, 16, SATTN_TOPK, 64, 0, 0.1f, I, I, 64, nullptr),
+         SATTN_ERR_UNSUPPORTED);                                                 // one head exceeds the scratch
+  EXPECT(sattn_mask_noalloc(P, P, 1, 2, 300, 500, 128, 64, SATTN_THRESH, 0, 2.0f, 0.1f, I, I, 500, nullptr), SATTN_ERR_ARG);
+  EXPECT(sattn_mask_noalloc(nullptr, P, 1, 2, 300, 500, 128, 64, SATTN_TOPK, 10, 0, 0.1f, I, I, 10, nullptr), SATTN_ERR_NULL);
   EXPECT(sattn_colsum_mask(P, P, nullptr, 1, 2, 300, 500, 128, 64, 10, 0.1f, I, I, 10, P, ws, nullptr), SATTN_ERR_NULL);
   EXPECT(sattn_cached_mask(P, P, F, 1, 2, 300, 500, 128, 64, 1e-3f, 0.1f, I, I, 500, nullptr), SATTN_ERR_HIP);
   EXPECT(sattn_cached_mask(P, P, F, 1, 2, 300, 500, 128, 64, 0.0f / 0.0f, 0.1f, I, I, 500, nullptr), SATTN_ERR_ARG);

@@ -17,6 +17,10 @@ int validate_index_lists(const int32_t*, const int32_t*, int, int, int, void*, i
   return FAKE_HIP_ERROR;
 }
 int launch_mask(const MaskArgs&) { ++g_launches; return FAKE_HIP_ERROR; }
+int launch_mask_noalloc(const MaskArgs&, int heads_per_call) {
+  ++g_launches;
+  return heads_per_call >= 1 ? FAKE_HIP_ERROR : 1;
+}
 int launch_cached_mask(const CachedMaskArgs&) { ++g_launches; return FAKE_HIP_ERROR; }
 int launch_colsum_scores(const ColsumArgs&) { ++g_launches; return FAKE_HIP_ERROR; }
 int launch_vsmooth(const VsmoothArgs&) { ++g_launches; return FAKE_HIP_ERROR; }
