@@ -11,9 +11,12 @@ from synth import inputs
 # Parity bar on the fp32 output given identical index lists.
 MAX_ABS = 1e-2
 REL_L2 = 5e-3
-# lse = m ln2 + ln(l), where l sums the bf16-rounded probabilities (each within 2^-9 relative), so its
-# error is bounded by about 2^-9; allow two bf16 half-ulps of slack.
-LSE_ABS = 4e-3
+# lse = m ln2 + ln(l), where l sums the bf16-rounded probabilities.  bf16 has 8 significant bits, so its
+# unit roundoff is 2^-8: each rounded probability is within 2^-8 of its exact value relative, l within
+# 2^-8 of the exact sum, and |ln l - ln l_exact| <= -ln(1 - 2^-8) = 3.914e-3; the fp32 arithmetic of
+# m ln2 + ln l adds below 1e-5 for |lse| < 100.
+LSE_ABS = 3.93e-3
+LSE_ERRORS = []      # (what, max |lse - oracle|) of every check, reported at the end of the session
 # mask key sets may differ only on keys whose oracle score is this close (logit scale) to the cut
 MASK_BAND = 1e-3
 
@@ -54,6 +57,7 @@ def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str):
     assert np.array_equal(np.isneginf(l_gpu), ninf), f"{what}: -inf pattern of lse differs"
     if (~ninf).any():
         err = np.abs(l_gpu[~ninf] - l_ref[~ninf]).max()
+        LSE_ERRORS.append((what, float(err)))
         assert err <= LSE_ABS, f"{what}: lse max|err| {err:.3g}"
 
 
