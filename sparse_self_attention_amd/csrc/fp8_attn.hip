@@ -468,25 +468,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
       skey = ilist[p < c ? p : c - 1];
     }
   };
+  // gathered indices are clamped to Nk: any out-of-range list value reads the zero row past the buffer end
   auto issue = [&](char* stage) {
 #pragma unroll
     for (int j = 0; j < NKS; ++j) {
       const int rs = wave + j * NW;
       if (L::KSETS % NW == 0 || rs < L::KSETS)
-        buffer_load_lds_x4(rk, stage + rs * L::RPL * L::RB, (uint32_t)kkeys[j] * L::RB + kch(j));
+        buffer_load_lds_x4(rk, stage + rs * L::RPL * L::RB, min((uint32_t)kkeys[j], (uint32_t)Nk) * L::RB + kch(j));
     }
 #pragma unroll
     for (int j = 0; j < NVS; ++j) {
       const int rs = wave + j * NW;
       if (L::VSETS % NW == 0 || rs < L::VSETS)
-        buffer_load_lds_x4(rv, stage + L::KBYTES + rs * L::RPL8 * D, (uint32_t)vkeys[j] * D + vch(j));
+        buffer_load_lds_x4(rv, stage + L::KBYTES + rs * L::RPL8 * D, min((uint32_t)vkeys[j], (uint32_t)Nk) * D + vch(j));
     }
     if (wave < ISETS)
       buffer_load_lds_x4(ro, stage + L::KBYTES + L::VBYTES + wave * 1024,
                          (uint32_t)((ikey >> 7) & (F8_WIN - 1)) * 32u + 16u * (uint32_t)(lane & 1));
     if (QK4 && wave == swave)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, SATTN_LDS_PTR(void, stage + L::KSOFF), L::KSB,
-                                               (uint32_t)skey * L::KSB, 0, 0, 0);
+                                               min((uint32_t)skey, (uint32_t)Nk) * L::KSB, 0, 0, 0);
   };
   // the tile's listed key of this lane (lane = position in the tile), for the mean windows
   auto tile_key = [&](int blk) {
