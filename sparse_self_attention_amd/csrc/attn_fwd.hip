@@ -194,8 +194,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     return t;
   };
 
-  auto block = [&](auto st, int j) {
+  auto block = [&](auto st, auto first, int j) {
     constexpr int ST = decltype(st)::value;
+    constexpr bool FIRST = decltype(first)::value != 0;   // block 0 sets the running max
     wait_vmcnt0();
     __syncthreads();
     if (j + 1 < nblk) {
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
         pk[r >> 1] = pack_bf16x2(p0, p1);
       }
     };
-    if (!DELTA && j == 0) take_max();
+    if (!DELTA && FIRST) take_max();
     exps();
     if (!DELTA) {
       // largest probability of the lane, as bf16 bits, by packed 16-bit integer maxima
@@ -285,12 +286,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     issue(sk0, sv0);
     if (nblk > 1) fetch_keys(1);
   }
-  int j = 0;
+  if (nblk > 0) block(IC<0>{}, IC<1>{}, 0);
+  int j = 1;
   for (; j + 1 < nblk; j += 2) {
-    block(IC<0>{}, j);
-    block(IC<1>{}, j + 1);
+    block(IC<1>{}, IC<0>{}, j);
+    block(IC<0>{}, IC<0>{}, j + 1);
   }
-  if (j < nblk) block(IC<0>{}, j);
+  if (j < nblk) block(IC<1>{}, IC<0>{}, j);
 
   if constexpr (DELTA) {
     if (row_valid) {
