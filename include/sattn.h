@@ -161,7 +161,8 @@ int sattn_cached_mask(const void* q, const void* k, const float* lse,
  * computed with bf16 inputs, fp32 accumulation and an fp32 online softmax (LongLive DiT blog,
  * "Online Softmax").  The probabilities enter P.V rounded to bf16 and the normaliser sums those
  * same rounded values, so out is exactly their weighted mean of V (error within the stated
- * 1e-2 max-abs / 5e-3 rel-L2 of the exact result; lse within about 2^-9).  A group with c = 0
+ * 1e-2 max-abs / 5e-3 rel-L2 of the exact result; lse within -ln(1 - 2^-8) = 3.9e-3, the bf16
+ * rounding of the summed probabilities).  A group with c = 0
  * gets out = 0 and lse = -inf.
  *
  *   q bf16 [B,H,Nq,D]; k, v bf16 [B,H,Nk,D]
