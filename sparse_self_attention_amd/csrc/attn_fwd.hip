@@ -116,6 +116,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
   const int32_t* ilist = DENSE ? nullptr : idx + ((size_t)bh * G + g) * (size_t)cap;
+  // the list through a buffer resource: 32-bit offsets, no 64-bit address arithmetic per load
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(ilist, DENSE ? 0u : (uint32_t)c * 4u);
 
   bf16x8 qf[L::KSTEPS];
   {
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
       const int p = blk * BKL + rs * L::ROWS_PER_LOAD + row_in;
       if (DENSE) keys[j] = p < Nk ? p : Nk - 1;
       else if (L::ROWSETS % NW == 0 || rs < L::ROWSETS)
-        keys[j] = ilist[p < c ? p : c - 1];
+        keys[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)min(p, c - 1) * 4u, 0, 0);
     }
   };
   auto issue = [&](char* kst, char* vst) {

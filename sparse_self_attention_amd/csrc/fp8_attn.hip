@@ -402,6 +402,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(vmean + (size_t)bh * D * nbp, (uint32_t)(D * nbp * 2));
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(k_onehot.b, (uint32_t)sizeof(k_onehot.b));
   const int32_t* ilist = idx + ((size_t)bh * G + g) * (size_t)cap;
+  // the list through a buffer resource: 32-bit offsets, no 64-bit address arithmetic per load
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(ilist, (uint32_t)c * 4u);
+  auto list_at = [&](int p) { return (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)min(p, c - 1) * 4u, 0, 0); };
 
   // the wave's query rows: bf16 (8 k-steps of 16 dims) or E2M1 (D/64 steps of 64 dims, 16 bytes a lane)
   constexpr int QREGS = QK4 ? D / 64 : L::KSTEPS;
@@ -451,21 +454,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     for (int j = 0; j < NKS; ++j) {
       const int rs = wave + j * NW;
       const int p = blk * F8_BK + rs * L::RPL + krow_in;
-      if (L::KSETS % NW == 0 || rs < L::KSETS) kkeys[j] = ilist[p < c ? p : c - 1];
+      if (L::KSETS % NW == 0 || rs < L::KSETS) kkeys[j] = list_at(p);
     }
 #pragma unroll
     for (int j = 0; j < NVS; ++j) {
       const int rs = wave + j * NW;
       const int p = blk * F8_BK + rs * L::RPL8 + vrow_in;
-      if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = ilist[p < c ? p : c - 1];
+      if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = list_at(p);
     }
     if (wave < ISETS) {
       const int p = blk * F8_BK + irow;
-      ikey = ilist[p < c ? p : c - 1];
+      ikey = list_at(p);
     }
     if (QK4 && wave == swave) {
       const int p = blk * F8_BK + lane;
-      skey = ilist[p < c ? p : c - 1];
+      skey = list_at(p);
     }
   };
   // gathered indices are clamped to Nk: any out-of-range list value reads the zero row past the buffer end
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   // the tile's listed key of this lane (lane = position in the tile), for the mean windows
   auto tile_key = [&](int blk) {
     const int p = blk * F8_BK + lane;
-    return p < c ? ilist[p] : -1;
+    return p < c ? list_at(p) : -1;
   };
 
   f32x16 o[L::DBLK];
