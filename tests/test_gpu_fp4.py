@@ -9,9 +9,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out, f64, onehot_case, onehot_total_variation,
-                      oracle_mx4_head, oracle_vsmooth_head, scale_of, structured_lists, to_device_bf16, value_ranges,
-                      vsmooth_to_device, workload)
+from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out_fp8, f64, onehot_case,
+                      onehot_total_variation, oracle_mx4_head, oracle_vsmooth_head, scale_of, structured_lists,
+                      to_device_bf16, value_ranges, vsmooth_to_device, workload)
 from synth import inputs
 
 pytestmark = pytest.mark.gpu
@@ -85,14 +85,14 @@ def _run(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0):
     out, lse = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
     torch.cuda.synchronize()
     what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
-    check_out(out.cpu().numpy(), ro, what)
+    check_out_fp8(out.cpu().numpy(), ro, vm, what)
     check_lse(lse.cpu().numpy(), rl, what)
     # the exact restricted softmax over the dequantised queries, keys and values, to the ExpCast bound
     vhat = oracle.dequantize_ref(vc, vs, vm)
     eo, el = oracle.sparse_attention_ref(oracle.mx4_dequantize_ref(qc, qe), oracle.mx4_dequantize_ref(kc, ke), vhat,
                                          idx, counts, group, scale)
     check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
-                        what + " vs exact softmax")
+                        what + " vs exact softmax", mean_abs_max=float(np.abs(vm).max()))
 
 
 FWD_CASES = [
@@ -145,7 +145,7 @@ def test_fp4_full_size_sampled(sattn):
         r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
         ro, rl = oracle.fp4_attention_ref(qc[:, :, r], qe[:, :, r], kc, ke, vc, vs, vm, idx[:, :1, g:g + 1],
                                           counts[:, :1, g:g + 1], w.group, scale)
-        check_out(out_h[:, :1, r], ro, f"long_70200 fp4 g={g}")
+        check_out_fp8(out_h[:, :1, r], ro, vm, f"long_70200 fp4 g={g}")
         check_lse(lse_h[:, :1, r], rl, f"long_70200 fp4 g={g}")
 
 
@@ -204,19 +204,20 @@ def test_fp4_full_size_exact_softmax(sattn):
             q4[:, h:h + 1, r].copy_(torch.from_numpy(a).to(DEV))
             qs[:, h:h + 1, r].copy_(torch.from_numpy(b).to(DEV))
             qrows[g] = oracle.mx4_dequantize_ref(qc, qe)
-        ref[h] = (oracle.mx4_dequantize_ref(kc, ke), oracle.dequantize_ref(vc, vs, vm), qrows)
+        ref[h] = (oracle.mx4_dequantize_ref(kc, ke), oracle.dequantize_ref(vc, vs, vm), qrows, float(np.abs(vm).max()))
     out, lse = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, idx, counts, w.group, out_dtype=torch.float32)
     torch.cuda.synchronize()
     out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
     idx_h, cnt_h = idx.cpu().numpy(), counts.cpu().numpy()
     worst = 0.0
     for h in heads:
-        kh, vhat, qrows = ref[h]
+        kh, vhat, qrows, mean_max = ref[h]
         for g in groups:
             r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
             ui, uc = idx_h[:, h:h + 1, g:g + 1], cnt_h[:, h:h + 1, g:g + 1]
             eo, el = oracle.sparse_attention_ref(qrows[g], kh, vhat, ui, uc, w.group, scale_of(w.dim))
             vr = value_ranges(vhat, ui, uc, w.group, r.stop - r.start)
             worst = max(worst, check_expcast_bound(out_h[:, h:h + 1, r], lse_h[:, h:h + 1, r], eo, el, vr,
-                                                   f"long_70200 fp4 h={h} g={g} vs exact softmax"))
+                                                   f"long_70200 fp4 h={h} g={g} vs exact softmax",
+                                                   mean_abs_max=mean_max))
     print(f"long_70200 FP4-score forward: worst |out - exact| at {worst:.3f} of the ExpCast bound")

@@ -10,9 +10,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out, f64, onehot_case, onehot_total_variation,
-                      oracle_vsmooth_head, scale_of, structured_lists, to_device_bf16, value_ranges, vsmooth_to_device,
-                      workload)
+from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out_fp8, f64, onehot_case,
+                      onehot_total_variation, oracle_vsmooth_head, scale_of, structured_lists, to_device_bf16,
+                      value_ranges, vsmooth_to_device, workload)
 from synth import inputs
 
 pytestmark = pytest.mark.gpu
@@ -91,13 +91,13 @@ def _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0, zero_group=Tr
     out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
     torch.cuda.synchronize()
     what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
-    check_out(out.cpu().numpy(), ro, what)
+    check_out_fp8(out.cpu().numpy(), ro, rm, what)
     check_lse(lse.cpu().numpy(), rl, what)
     # the exact restricted softmax over the same dequantised values, to the summary's ExpCast bound
     vhat = oracle.dequantize_ref(rc, rs, rm)
     eo, el = oracle.sparse_attention_ref(f64(qb), f64(kb), vhat, idx, counts, group, scale)
     check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
-                        what + " vs exact softmax")
+                        what + " vs exact softmax", mean_abs_max=float(np.abs(rm).max()))
     if zero_group and G > 1:
         r = slice((G - 1) * group, Nq)
         assert not out[0, 1, r].any().item() and torch.isneginf(lse[0, 1, r]).all().item()
@@ -187,7 +187,8 @@ def test_fp8_full_size_exact_softmax(sattn):
                                                  scale)
             vr = value_ranges(vhat, ui, uc, w.group, r.stop - r.start)
             worst = max(worst, check_expcast_bound(out_h[:, h:h + 1, r], lse_h[:, h:h + 1, r], eo, el, vr,
-                                                   f"long_70200 fp8 h={h} g={g} vs exact softmax"))
+                                                   f"long_70200 fp8 h={h} g={g} vs exact softmax",
+                                                   mean_abs_max=float(np.abs(quant[h][2]).max())))
     print(f"long_70200 FP8 forward: worst |out - exact| at {worst:.3f} of the ExpCast bound")
 
 
@@ -220,5 +221,5 @@ def test_fp8_full_size_sampled(sattn):
         ui = idx[:, :1, g:g + 1]
         uc = counts[:, :1, g:g + 1]
         ro, rl = oracle.fp8_attention_ref(f64(qb[:, :1, r]), f64(kb[:, :1]), rc, rs, rm, ui, uc, w.group, scale)
-        check_out(out_h[:, :1, r], ro, f"long_70200 fp8 g={g}")
+        check_out_fp8(out_h[:, :1, r], ro, rm, f"long_70200 fp8 g={g}")
         check_lse(lse_h[:, :1, r], rl, f"long_70200 fp8 g={g}")

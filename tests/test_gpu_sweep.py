@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (MASK_BAND, check_lse, check_mask_sets, check_out, check_out_scaled, f64, scale_of,
-                      structured_lists, to_device_bf16, vsmooth_to_device)
+from gpu_util import (MASK_BAND, check_lse, check_mask_sets, check_out, check_out_fp8, check_out_scaled, f64,
+                      scale_of, structured_lists, to_device_bf16, vsmooth_to_device)
 from synth import inputs
 from test_gpu_cached import check_cached_sets
 from test_gpu_delta import LOG_BAND, _check_colsum_sets
@@ -203,7 +203,7 @@ def test_fp8_forward(sattn, case):
     out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, torch.from_numpy(idx).to(DEV),
                                  torch.from_numpy(counts).to(DEV), group, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    check_out(out.cpu().numpy(), ro, f"fp8 sweep {i}")
+    check_out_fp8(out.cpu().numpy(), ro, rm, f"fp8 sweep {i}")
     check_lse(lse.cpu().numpy(), rl, f"fp8 sweep {i}")
 
 
