@@ -49,7 +49,7 @@ def _draw_cases(n, seed=2024):
     return cases
 
 
-CASES = _draw_cases(24)
+CASES = _draw_cases(36)
 
 
 @pytest.fixture(scope="module")
@@ -80,14 +80,14 @@ def _ids(cases):
 
 
 STD = lambda rng: float(rng.choice([1.0, 2.0, 4.0]))
-DENSE_CASES = _draw_list(np.random.default_rng(7001), 9, lambda rng, D, g, nq, nk: (STD(rng),))
-CACHED_CASES = _draw_list(np.random.default_rng(7002), 9, lambda rng, D, g, nq, nk: (
+DENSE_CASES = _draw_list(np.random.default_rng(7001), 12, lambda rng, D, g, nq, nk: (STD(rng),))
+CACHED_CASES = _draw_list(np.random.default_rng(7002), 12, lambda rng, D, g, nq, nk: (
     float(10.0 ** rng.uniform(-5.0, -1.0)) if rng.random() < 0.5 else 0.5 / nk, STD(rng)))
-COLSUM_CASES = _draw_list(np.random.default_rng(7003), 9, lambda rng, D, g, nq, nk: (
+COLSUM_CASES = _draw_list(np.random.default_rng(7003), 12, lambda rng, D, g, nq, nk: (
     int(rng.integers(1, nk + 1)), int(rng.integers(1, nk + 1)), STD(rng)))
-FP8_CASES = _draw_list(np.random.default_rng(7004), 9, lambda rng, D, g, nq, nk: (
+FP8_CASES = _draw_list(np.random.default_rng(7004), 12, lambda rng, D, g, nq, nk: (
     int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
-FP4_CASES = _draw_list(np.random.default_rng(7005), 9, lambda rng, D, g, nq, nk: (
+FP4_CASES = _draw_list(np.random.default_rng(7005), 12, lambda rng, D, g, nq, nk: (
     int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
 
 
