@@ -65,3 +65,32 @@ def test_noalloc_rejects_a_head_larger_than_the_scratch(sattn):
     with pytest.raises(sattn.SattnError) as e:
         sattn.mask_noalloc(q, k, 16, topk=64, idx=idx, counts=cnt)
     assert e.value.status == 3
+
+
+def test_noalloc_mask_in_a_graph(sattn):
+    """The caller the entry point is for: sattn_mask_noalloc captured into a HIP graph (no workspace to
+    allocate), replayed three times with eager work between the replays; every replay's lists equal the
+    eager sattn_mask's bit for bit."""
+    rng = np.random.default_rng(104)
+    group, topk = 128, 700
+    q, k = _qk(rng, 1, 3, 1000, 5000, 128)
+    ref_idx, ref_cnt = sattn.mask(q, k, group, topk=topk)
+    idx = torch.empty_like(ref_idx)
+    cnt = torch.empty_like(ref_cnt)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sattn.mask_noalloc(q, k, group, topk=topk, idx=idx, counts=cnt)     # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sattn.mask_noalloc(q, k, group, topk=topk, idx=idx, counts=cnt)
+    for rep in range(3):
+        idx.fill_(-7)                  # eager work between the replays
+        cnt.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cnt, ref_cnt), f"replay {rep}: counts differ"
+        assert torch.equal(idx, ref_idx), f"replay {rep}: lists differ"
