@@ -83,8 +83,9 @@ constexpr int SC_KT = 16;   // 32-key tiles per workgroup
 
 // S = q_avg K^T: A = 32 group means (rows = groups, hi and lo halves in VGPRs), B = K^T (columns =
 // keys).  The 4 waves of a workgroup own 4 different 32-group tiles and walk the same SC_KT x 32
-// keys; each 32-key tile is gathered once into LDS with buffer-load-to-LDS (double-buffered, rows
-// XOR-swizzled as in the forward) and read by all four waves.  In the accumulator layout lane l holds
+// keys; each 64-key tile is gathered once into LDS with buffer-load-to-LDS (double-buffered, rows
+// XOR-swizzled as in the forward) and read by all four waves as two 32-key MFMA tiles (with 32-key
+// tiles the next tile's gather did not land within one tile's work: 7 % slower per mask call).  In the accumulator layout lane l holds
 // key j0 + l%32 for 16 groups: each store instruction writes two contiguous 128-byte runs of score
 // rows.
 template <int D>
@@ -96,9 +97,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   constexpr int RB = D * 2;
   constexpr int NC = D / 8;                       // 16-byte chunks per row
   constexpr int ROWS_PER_LOAD = 1024 / RB;        // rows filled by one 64-lane 16-byte load
-  constexpr int ROWSETS = 32 / ROWS_PER_LOAD;
+  constexpr int TKEYS = 64;                       // keys per LDS tile: two 32-key MFMA tiles
+  constexpr int ROWSETS = TKEYS / ROWS_PER_LOAD;
   constexpr int NRS = (ROWSETS + 3) / 4;          // row-sets gathered per wave
-  constexpr int TILE = 32 * RB;
+  constexpr int TILE = TKEYS * RB;
   constexpr int ROWDIV = 16 / NC;
   __shared__ __attribute__((aligned(1024))) char ktile[2 * TILE];
   // this workgroup's samples (SC_KT * 32 / SAMPLE_STEP per group), stored as whole runs at the end
@@ -135,13 +137,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
   for (int j = 0; j < NRS; ++j) kch[j] = 16u * (uint32_t)(pchunk ^ swz((wave + 4 * j) * ROWS_PER_LOAD + row_in));
   const int jbase = kc * SC_KT * 32;
-  const int ntile = min(SC_KT, (Nk - jbase + 31) / 32);
+  const int ntile = min(SC_KT * 32 / TKEYS, (Nk - jbase + TKEYS - 1) / TKEYS);
   auto issue = [&](int st, int tile) {
 #pragma unroll
     for (int j = 0; j < NRS; ++j) {
       const int rs = wave + 4 * j;
       if (ROWSETS % 4 == 0 || rs < ROWSETS) {
-        const int p = jbase + tile * 32 + rs * ROWS_PER_LOAD + row_in;
+        const int p = jbase + tile * TKEYS + rs * ROWS_PER_LOAD + row_in;
         const uint32_t key = (uint32_t)(p < Nk ? p : Nk - 1);
         buffer_load_lds_x4(rk, ktile + st * TILE + rs * ROWS_PER_LOAD * RB, key * RB + kch[j]);
       }
@@ -160,23 +162,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     __syncthreads();   // tile landed for every wave; the other stage is free again
     if (tile + 1 < ntile) issue((tile + 1) & 1, tile + 1);
     if (!active) continue;
-    const char* kt = ktile + (tile & 1) * TILE;
-    f32x16 acc = {};
+    // the tile's two 32-key halves in turn (rows 32 + r carry the same swizzle as rows r)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 b = *(const bf16x8*)(kt + koff[ks]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], b, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], b, acc, 0, 0, 0);
-    }
-    const int j = jbase + tile * 32 + ql;
-    if (j < Nk) {
+    for (int sub = 0; sub < TKEYS / 32; ++sub) {
+      const char* kt = ktile + (tile & 1) * TILE + sub * 32 * RB;
+      f32x16 acc = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int g = gt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (g < G) {
-          const float sv = acc[r] * scale;
-          sbase[(size_t)g * stride + j] = sv;
-          if (sampler) ssamp[(g - gq * 128) * SPW + (j - jbase) / SAMPLE_STEP] = sv;
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 b = *(const bf16x8*)(kt + koff[ks]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], b, acc, 0, 0, 0);
+      }
+      const int j = jbase + tile * TKEYS + sub * 32 + ql;
+      if (j < Nk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int g = gt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (g < G) {
+            const float sv = acc[r] * scale;
+            sbase[(size_t)g * stride + j] = sv;
+            if (sampler) ssamp[(g - gq * 128) * SPW + (j - jbase) / SAMPLE_STEP] = sv;
+          }
         }
       }
     }
