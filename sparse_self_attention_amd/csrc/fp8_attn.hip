@@ -341,6 +341,14 @@ __device__ __attribute__((aligned(256))) const OneHotTable k_onehot = make_oneho
 // eight rows one transposing read touches ({0..3, 8..11} + 4h) cover all 64 banks.  An involution.
 __device__ inline int ind_pos(int r) { return r ^ ((r & 8) >> 1); }
 
+// The lane id from v_mbcnt, behind an asm barrier so the compiler cannot hoist it out of a loop into a
+// register that lives (and may be spilled) across the loop.
+__device__ inline int opaque_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // ExpCast: the float bits clamped so that the low byte is the code, 0..127 (0x4B400000 = 1.5 * 2^23
 // holds 0; 127 flags a byte past the largest finite code)
 __device__ inline uint32_t expcast_bits(float s, float c1, float c0) {
@@ -376,7 +384,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   constexpr int NVS = (L::VSETS + NW - 1) / NW;
   constexpr int ISETS = L::IBYTES / 1024;          // slot-row loads per tile (2)
   static_assert(NW >= ISETS, "one slot-row load per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
+  // Each stage's K, V and slot-row tiles are LDS objects of their own, so the compiler can tell that the
+  // reads of one stage do not depend on the gather in flight into the other one (no wait for it).
+  __shared__ __attribute__((aligned(1024))) char sk0[L::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sv0[L::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char si0[L::IBYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[L::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sv1[L::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char si1[L::IBYTES];
 
   const uint32_t unit = xcd_striped(blockIdx.x, n_units, 128);
   const int g = (int)(unit % (uint32_t)G);
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   const uint32_t vbase = vrow * D + 16 * (g16 & 1) + 8 * (j16 & 1);
   const int vswz = L::swz_v(vrow);
   auto voff = [&](int db) { return vbase + 32u * (uint32_t)(db ^ vswz); };
-  const uint32_t ioff = L::KBYTES + L::VBYTES + ind_pos(vrow) * 32 + 16 * (g16 & 1) + 8 * (j16 & 1);
+  const uint32_t ioff = ind_pos(vrow) * 32 + 16 * (g16 & 1) + 8 * (j16 & 1);
 
   const int krow_in = lane / L::NC, kpos = lane % L::NC;
   const int vrow_in = lane / L::NC8, vpos = lane % L::NC8;
@@ -445,8 +460,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     return 16u * (uint32_t)(2 * ((vpos >> 1) ^ L::swz_v(row)) + (vpos & 1));
   };
   // slot-row load of this wave (waves 0 and 1): LDS position 32 wave + lane / 2 holds key row
-  // ind_pos(position), chunk lane % 2
-  const int irow = ind_pos(32 * wave + (lane >> 1));
+  // ind_pos(position), chunk lane % 2.  The row is recomputed from the lane id at each fetch: held across
+  // the loop it would be spilled, and its reload right after the gather is issued waits for that gather.
+  auto irow = [&]() { return ind_pos(32 * wave + (opaque_lane_id() >> 1)); };
   int kkeys[NKS], vkeys[NVS], ikey = 0, skey = 0;
   const int swave = NW - 1;        // the wave that gathers the keys' E8M0 scales (4-bit product)
   auto fetch_keys = [&](int blk) {
@@ -463,7 +479,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
       if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = list_at(p);
     }
     if (wave < ISETS) {
-      const int p = blk * F8_BK + irow;
+      const int p = blk * F8_BK + irow();
       ikey = list_at(p);
     }
     if (QK4 && wave == swave) {
@@ -472,24 +488,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     }
   };
   // gathered indices are clamped to Nk: any out-of-range list value reads the zero row past the buffer end
-  auto issue = [&](char* stage) {
+  auto issue = [&](char* kst, char* vst, char* ist) {
 #pragma unroll
     for (int j = 0; j < NKS; ++j) {
       const int rs = wave + j * NW;
       if (L::KSETS % NW == 0 || rs < L::KSETS)
-        buffer_load_lds_x4(rk, stage + rs * L::RPL * L::RB, min((uint32_t)kkeys[j], (uint32_t)Nk) * L::RB + kch(j));
+        buffer_load_lds_x4(rk, kst + rs * L::RPL * L::RB, min((uint32_t)kkeys[j], (uint32_t)Nk) * L::RB + kch(j));
     }
 #pragma unroll
     for (int j = 0; j < NVS; ++j) {
       const int rs = wave + j * NW;
       if (L::VSETS % NW == 0 || rs < L::VSETS)
-        buffer_load_lds_x4(rv, stage + L::KBYTES + rs * L::RPL8 * D, min((uint32_t)vkeys[j], (uint32_t)Nk) * D + vch(j));
+        buffer_load_lds_x4(rv, vst + rs * L::RPL8 * D, min((uint32_t)vkeys[j], (uint32_t)Nk) * D + vch(j));
     }
     if (wave < ISETS)
-      buffer_load_lds_x4(ro, stage + L::KBYTES + L::VBYTES + wave * 1024,
+      buffer_load_lds_x4(ro, ist + wave * 1024,
                          (uint32_t)((ikey >> 7) & (F8_WIN - 1)) * 32u + 16u * (uint32_t)(lane & 1));
     if (QK4 && wave == swave)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, SATTN_LDS_PTR(void, stage + L::KSOFF), L::KSB,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, SATTN_LDS_PTR(void, kst + L::KSOFF), L::KSB,
                                                min((uint32_t)skey, (uint32_t)Nk) * L::KSB, 0, 0, 0);
   };
   // the tile's listed key of this lane (lane = position in the tile), for the mean windows
@@ -535,18 +551,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     slot_hi = -1;
   };
 
-  auto block = [&](int j) {
-    const int ST = j & 1;
+  auto block = [&](auto st, int j) {
+    constexpr int ST = decltype(st)::value;
     wait_vmcnt0();
     __syncthreads();
     const int key_here = tkey;
     if (j + 1 < nblk) {
-      issue(smem + (1 - ST) * L::STAGE);
+      if (ST == 0) issue(sk1, sv1, si1);
+      else issue(sk0, sv0, si0);
       if (j + 2 < nblk) fetch_keys(j + 2);
       tkey = tile_key(j + 1);
     }
-    const char* sk = smem + ST * L::STAGE;
-    const char* sv = sk + L::KBYTES;
+    const char* sk = ST == 0 ? sk0 : sk1;
+    const char* sv = ST == 0 ? sv0 : sv1;
+    const char* si = ST == 0 ? si0 : si1;
     f32x16 s0 = {}, s1 = {};
     if constexpr (QK4) {
       // E8M0 scales of keys ql and 32 + ql, shifted so byte 2t holds block 2t + hi
@@ -635,7 +653,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
     }
     i32x8 ia;
     {
-      const char* p0 = sk + ioff;
+      const char* p0 = si + ioff;
       const i32x2v t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0));
       const i32x2v t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 512));
       const i32x2v t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(SATTN_LDS_PTR(i32x2v, p0 + 1024));
@@ -671,11 +689,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
 
   if (nblk > 0) {
     fetch_keys(0);
-    issue(smem);
+    issue(sk0, sv0, si0);
     if (nblk > 1) fetch_keys(1);
     tkey = tile_key(0);
   }
-  for (int j = 0; j < nblk; ++j) block(j);
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    block(F8IC<0>{}, j);
+    block(F8IC<1>{}, j + 1);
+  }
+  if (j < nblk) block(F8IC<0>{}, j);
   if (nblk > 0) flush();
 
   const float l_tot = pair_sum(l_run);
