@@ -32,6 +32,8 @@
 // order) and stores the fp32 sums in the staging layout that the top-k selection reads.
 #include <math.h>
 
+#include <type_traits>
+
 #include "../../include/sattn.h"
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -42,6 +44,9 @@ namespace sattn {
 namespace {
 
 constexpr int CM_BK = 32;   // keys per block
+
+template <int N>
+using CmIC = std::integral_constant<int, N>;
 
 template <int D>
 struct CmLayout {
@@ -94,7 +99,10 @@ __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restr
   using L = CmLayout<D>;
   constexpr int NT = NW * 64;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
-  __shared__ __attribute__((aligned(1024))) char stage[2 * L::STAGE_BYTES];
+  // The two stages are LDS objects of their own, so the compiler can tell that the reads of one stage
+  // do not depend on the gather in flight into the other one (no wait for it).
+  __shared__ __attribute__((aligned(1024))) char sk0[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[L::STAGE_BYTES];
   __shared__ int wsum[NW];
   __shared__ float part[COLSUM ? 2 : 1][NW][32];
   extern __shared__ uint32_t bm[];
@@ -171,15 +179,15 @@ __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restr
     }
   };
 
-  issue(stage, 0);
-  for (int j = 0; j < nblk; ++j) {
-    const int st = j & 1;
+  // block j reads stage j % 2 (even blocks stage 0)
+  auto block = [&](auto stc, int j) {
+    constexpr int st = decltype(stc)::value;
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt0();
     __syncthreads();   // stage j landed for every wave; stage j+1 is free again
-    if (j + 1 < nblk) issue(stage + (1 - st) * L::STAGE_BYTES, j + 1);
+    if (j + 1 < nblk) issue(st == 0 ? sk1 : sk0, j + 1);
     if (COLSUM && j > 0) flush(j - 1);   // every wave's partial of block j-1 is in LDS
-    const char* sk = stage + st * L::STAGE_BYTES;
+    const char* sk = st == 0 ? sk0 : sk1;
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks) {
@@ -201,7 +209,14 @@ __global__ __launch_bounds__(NW * 64) void k_cached_mask(const uint16_t* __restr
       const uint64_t keep = __builtin_amdgcn_ballot_w64(valid && mx >= log2_tau);
       if (lane == 0 && (uint32_t)keep != 0u) atomicOr(&bm[j], (uint32_t)keep);
     }
+  };
+  issue(sk0, 0);
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    block(CmIC<0>{}, j);
+    block(CmIC<1>{}, j + 1);
   }
+  if (j < nblk) block(CmIC<0>{}, j);
   __syncthreads();
   if constexpr (COLSUM) {
     flush(nblk - 1);
