@@ -360,18 +360,15 @@ static inline size_t select_lds_bytes(int Nk, bool topk) {
   return 4 * ((topk ? 4096 : 0) + 2 * 8 * chunks + 2 * chunks + (topk ? 2 * SEL_CAND : 0));
 }
 
-// Order keys of keys i*SEL_ROW + 4*tid + e, e = 0..3 (0 past Nk).  Score rows are padded to a multiple of
-// 32 floats, so the 16-byte load of a partly valid quad stays inside its row.
-__device__ inline void keys4(const float* srow, int i, int tid, int Nk, uint32_t (&u)[SEL_KPT]) {
+// Order keys of keys i*SEL_ROW + 4*tid + e, e = 0..3 (0 past Nk).  The score row is read through a
+// buffer resource (loads past its end return zeros), so the load carries no branch and a batch of them
+// is in flight at once; score rows are padded to a multiple of 32 floats, so a partly valid quad stays
+// inside its row.
+__device__ inline void keys4(__amdgpu_buffer_rsrc_t rs, int i, int tid, int Nk, uint32_t (&u)[SEL_KPT]) {
   const int j = i * SEL_ROW + SEL_KPT * tid;
-  if (j < Nk) {
-    const f32x4 s = *(const f32x4*)(srow + j);
+  const f32x4 s = __builtin_bit_cast(f32x4, buffer_load_x4(rs, (uint32_t)j * 4u));
 #pragma unroll
-    for (int e = 0; e < SEL_KPT; ++e) u[e] = j + e < Nk ? order_key(s[e]) : 0u;
-  } else {
-#pragma unroll
-    for (int e = 0; e < SEL_KPT; ++e) u[e] = 0u;
-  }
+  for (int e = 0; e < SEL_KPT; ++e) u[e] = j + e < Nk ? order_key(s[e]) : 0u;
 }
 
 // Bitmap word and bit of key j.
@@ -410,6 +407,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   const int hh = bid / G, g = bid % G;
   const size_t unit = ((size_t)bh0 + hh) * G + g;
   const float* srow = scores + ((size_t)hh * G + g) * score_stride(Nk);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (uint32_t)score_stride(Nk) * 4u);
   const int rows = (Nk + SEL_ROW - 1) / SEL_ROW;
   const int chunks = rows * SEL_WAVES;
   const int words = 8 * chunks;
@@ -469,7 +467,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
       uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(rs, i0 + r, tid, Nk, u[r]);
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r) {
         const int i = i0 + r;
@@ -556,7 +554,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
           uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-          for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
+          for (int r = 0; r < SEL_BATCH; ++r) keys4(rs, i0 + r, tid, Nk, u[r]);
 #pragma unroll
           for (int r = 0; r < SEL_BATCH; ++r)
 #pragma unroll
@@ -573,7 +571,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       need = kk;
       for (int i = 0; i < rows; ++i) {
         uint32_t u[SEL_KPT];
-        keys4(srow, i, tid, Nk, u);
+        keys4(rs, i, tid, Nk, u);
         uint64_t st[SEL_KPT], ti[SEL_KPT];
 #pragma unroll
         for (int e = 0; e < SEL_KPT; ++e) {
@@ -591,7 +589,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
       uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(rs, i0 + r, tid, Nk, u[r]);
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r)
 #pragma unroll
@@ -603,7 +601,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
       uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(rs, i0 + r, tid, Nk, u[r]);
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r)
 #pragma unroll
@@ -617,7 +615,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
       uint32_t u[SEL_BATCH][SEL_KPT];
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r) keys4(srow, i0 + r, tid, Nk, u[r]);
+      for (int r = 0; r < SEL_BATCH; ++r) keys4(rs, i0 + r, tid, Nk, u[r]);
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r) {
         if (i0 + r < rows) {
@@ -666,7 +664,36 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   __syncthreads();
   int32_t* out = idx + unit * (size_t)cap;
   const int kept = tot_s + min(tot_t, need);
-  if (kept > 0) {
+  if (kept > 0 && tot_t <= need) {
+    // Every key at the cut is kept (the common case): a key is listed iff its strict or tie flag is
+    // set.  Lane l's keys 4l .. 4l+3 of a chunk land at consecutive positions after the chunk's base
+    // and the kept keys of lanes below l.  The stores go through a buffer resource over the list, so
+    // an unlisted key (or a position past cap) takes an offset past the end and is dropped: no branches.
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)cap * 4u);
+    const uint32_t lbit = 1u << (lane & 31);
+    for (int i = 0; i < rows; ++i) {
+      const int x = i * SEL_WAVES + wave;
+      const u32x4 s0 = *(const u32x4*)(strict_bits + 8 * x), s1 = *(const u32x4*)(strict_bits + 8 * x + 4);
+      const u32x4 t0 = *(const u32x4*)(tie_bits + 8 * x), t1 = *(const u32x4*)(tie_bits + 8 * x + 4);
+      const uint32_t w[8] = {s0[0] | t0[0], s0[1] | t0[1], s0[2] | t0[2], s0[3] | t0[3],
+                             s1[0] | t1[0], s1[1] | t1[1], s1[2] | t1[2], s1[3] | t1[3]};
+      int before = __builtin_amdgcn_readfirstlane(cnt_s[x] + cnt_t[x]);
+      uint32_t nib = 0;   // bit e: key 4l + e is listed
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e) {
+        before += (int)__builtin_amdgcn_mbcnt_hi(w[2 * e + 1], __builtin_amdgcn_mbcnt_lo(w[2 * e], 0u));
+        nib |= (((lane < 32 ? w[2 * e] : w[2 * e + 1]) & lbit) != 0u ? 1u : 0u) << e;
+      }
+      const uint32_t key0 = (uint32_t)(x * SEL_CHUNK + SEL_KPT * lane);
+#pragma unroll
+      for (int e = 0; e < SEL_KPT; ++e) {
+        const uint32_t pos = (uint32_t)before + (uint32_t)__builtin_popcount(nib & ((1u << e) - 1u));
+        __builtin_amdgcn_raw_buffer_store_b32(key0 + (uint32_t)e, ro, ((nib >> e) & 1u) ? pos * 4u : 0x80000000u, 0, 0);
+      }
+    }
+    if (tid == 0) counts[unit] = min(kept, cap);
+  } else if (kept > 0) {
+    // only the lowest-index `need` of the keys at the cut are kept
     for (int i = 0; i < rows; ++i) {
       const int x = i * SEL_WAVES + wave;
       uint64_t bs[SEL_KPT], bt[SEL_KPT];
@@ -697,7 +724,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     uint32_t best = 0;
     for (int i = 0; i < rows; ++i) {
       uint32_t u[SEL_KPT];
-      keys4(srow, i, tid, Nk, u);
+      keys4(rs, i, tid, Nk, u);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) best = u[e] > best ? u[e] : best;
     }
@@ -713,7 +740,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     int jmin = 0x7fffffff;
     for (int i = 0; i < rows; ++i) {
       uint32_t u[SEL_KPT];
-      keys4(srow, i, tid, Nk, u);
+      keys4(rs, i, tid, Nk, u);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e)
         if (u[e] == bmax && u[e] != 0u) jmin = min(jmin, i * SEL_ROW + SEL_KPT * tid + e);
