@@ -433,7 +433,20 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       const int S = sample_len(Nk);               // <= 2 * SEL_CAND: cand_key and cand_j are contiguous
       uint32_t* skey = cand_key;
       const float* prow = samples + ((size_t)hh * G + g) * sample_stride(Nk);
-      for (int x = tid; x < S; x += SEL_THREADS) skey[x] = order_key(prow[x]);
+      // two 16-byte loads a thread cover up to 8192 samples; both are in flight before either is used
+      static_assert(2 * SEL_CAND <= 8 * SEL_THREADS, "two sample quads a thread");
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(prow, (uint32_t)sample_stride(Nk) * 4u);
+      f32x4 sq[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        sq[t] = __builtin_bit_cast(f32x4, buffer_load_x4(rp, (uint32_t)(tid + t * SEL_THREADS) * 16u));
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * (tid + t * SEL_THREADS) + e;
+          if (x < S) skey[x] = order_key(sq[t][e]);
+        }
       for (int bb = tid; bb < 4096; bb += SEL_THREADS) hist[bb] = 0;
       __syncthreads();
       const double pk = (double)topk / (double)Nk;
@@ -463,22 +476,32 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     if (tid == 0) ncand = 0;
     __syncthreads();
     // ---- 2. one pass: keys above the band -> strict bits; keys in it -> LDS candidates ----
+    // The pass compares the scores as floats against the band's ends (the order keys' inverse images;
+    // an open end is an infinity): order_key is monotone and maps -0 and +0 to one key, as float
+    // comparison treats them.  Candidates keep their raw bits and are turned into order keys when the
+    // radix select reads them.  (A NaN score is never above or inside the band.)
+    // (keys from 0xFF800000 up are +inf and NaNs, keys up to 0x007FFFFF are -inf and NaNs)
+    const float hi_f = key_hi >= 0xFF800000u ? INFINITY : key_to_float(key_hi);
+    const float lo_f = key_lo <= 0x007FFFFFu ? -INFINITY : key_to_float(key_lo);
     int above_w = 0;   // keys above the band seen by this wave (uniform)
     for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
-      uint32_t u[SEL_BATCH][SEL_KPT];
+      f32x4 sv[SEL_BATCH];
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r) keys4(rs, i0 + r, tid, Nk, u[r]);
+      for (int r = 0; r < SEL_BATCH; ++r)
+        sv[r] = __builtin_bit_cast(f32x4, buffer_load_x4(rs, (uint32_t)((i0 + r) * SEL_ROW + SEL_KPT * tid) * 4u));
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r) {
         const int i = i0 + r;
         if (i < rows) {
           uint64_t ab[SEL_KPT], bc[SEL_KPT];
           int nb = 0;
+          const int j0 = i * SEL_ROW + SEL_KPT * tid;
 #pragma unroll
           for (int e = 0; e < SEL_KPT; ++e) {
-            const uint32_t x = u[r][e];
-            ab[e] = __builtin_amdgcn_ballot_w64(x > key_hi);
-            bc[e] = __builtin_amdgcn_ballot_w64(x != 0u && x >= key_lo && x <= key_hi);
+            const float x = sv[r][e];
+            const bool valid = j0 + e < Nk;
+            ab[e] = __builtin_amdgcn_ballot_w64(valid && x > hi_f);
+            bc[e] = __builtin_amdgcn_ballot_w64(valid && x >= lo_f && x <= hi_f);
             nb += (int)__popcll(bc[e]);
             above_w += (int)__popcll(ab[e]);
           }
@@ -492,8 +515,8 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
               if ((bc[e] >> lane) & 1u) {
                 const int pos = base + mbcnt64(bc[e]);
                 if (pos < SEL_CAND) {
-                  cand_key[pos] = u[r][e];
-                  cand_j[pos] = i * SEL_ROW + SEL_KPT * tid + e;
+                  cand_key[pos] = __float_as_uint(sv[r][e]);
+                  cand_j[pos] = j0 + e;
                 }
               }
               base += (int)__popcll(bc[e]);
@@ -522,7 +545,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         if (tid == 0) { found[0] = 0; found[1] = 1; }
         __syncthreads();
         for (int x = tid; x < nc; x += SEL_THREADS) {
-          const uint32_t u = cand_key[x];
+          const uint32_t u = order_key(__uint_as_float(cand_key[x]));
           if (((uint64_t)(u ^ prefix) >> bits) == 0) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
         }
         __syncthreads();
@@ -534,7 +557,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       }
       need = kk;
       for (int x = tid; x < nc; x += SEL_THREADS) {
-        const uint32_t u = cand_key[x];
+        const uint32_t u = order_key(__uint_as_float(cand_key[x]));
         const int jj = cand_j[x];
         if (u > prefix) atomicOr(&strict_bits[flag_word(jj)], flag_bit(jj));
         else if (u == prefix) atomicOr(&tie_bits[flag_word(jj)], flag_bit(jj));
