@@ -57,7 +57,7 @@ enum { SATTN_BF16 = 0, SATTN_F32 = 1 };      /* output dtype */
 /*
  * sattn_mask_workspace_bytes - device workspace that sattn_mask needs for these sizes.
  * Returns 0 if the sizes are invalid.  The workspace holds the group means and the fp32
- * mean-query scores of as many heads as fit in about 1 GB (at least one head), plus a
+ * mean-query scores of as many heads as fit in about 2 GB (at least one head), plus a
  * 1/16 sample of those scores.
  */
 size_t sattn_mask_workspace_bytes(int B, int H, int Nq, int Nk, int D, int group);

@@ -9,7 +9,7 @@
 //                 so the matrix cores score with about 16 mantissa bits of the mean.
 //  k_scores       s[g, j] = scale * (hi_g . k_j + lo_g . k_j) with v_mfma_f32_32x32x16_bf16, in tiles
 //                 of 128 groups x 32 keys so every K row read feeds 128 groups; fp32 scores of a bounded
-//                 number of heads are staged in the workspace (up to 1 GB, so one select launch
+//                 number of heads are staged in the workspace (up to 2 GB, so one select launch
 //                 spans several heads and fills the GPU).
 //  k_select       one 1024-thread workgroup per group.  Top-k: the scores kernel also writes every
 //                 16th score of a row to a short sample row; the sample's order statistics bracket
@@ -693,25 +693,22 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     // and the kept keys of lanes below l.  The stores go through a buffer resource over the list, so
     // an unlisted key (or a position past cap) takes an offset past the end and is dropped: no branches.
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)cap * 4u);
-    const uint32_t lbit = 1u << (lane & 31);
     for (int i = 0; i < rows; ++i) {
       const int x = i * SEL_WAVES + wave;
       const u32x4 s0 = *(const u32x4*)(strict_bits + 8 * x), s1 = *(const u32x4*)(strict_bits + 8 * x + 4);
       const u32x4 t0 = *(const u32x4*)(tie_bits + 8 * x), t1 = *(const u32x4*)(tie_bits + 8 * x + 4);
       const uint32_t w[8] = {s0[0] | t0[0], s0[1] | t0[1], s0[2] | t0[2], s0[3] | t0[3],
                              s1[0] | t1[0], s1[1] | t1[1], s1[2] | t1[2], s1[3] | t1[3]};
-      int before = __builtin_amdgcn_readfirstlane(cnt_s[x] + cnt_t[x]);
-      uint32_t nib = 0;   // bit e: key 4l + e is listed
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(cnt_s[x] + cnt_t[x]);
 #pragma unroll
-      for (int e = 0; e < SEL_KPT; ++e) {
-        before += (int)__builtin_amdgcn_mbcnt_hi(w[2 * e + 1], __builtin_amdgcn_mbcnt_lo(w[2 * e], 0u));
-        nib |= (((lane < 32 ? w[2 * e] : w[2 * e + 1]) & lbit) != 0u ? 1u : 0u) << e;
-      }
+      for (int e = 0; e < SEL_KPT; ++e) pos += __builtin_amdgcn_mbcnt_hi(w[2 * e + 1], __builtin_amdgcn_mbcnt_lo(w[2 * e], 0u));
       const uint32_t key0 = (uint32_t)(x * SEL_CHUNK + SEL_KPT * lane);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) {
-        const uint32_t pos = (uint32_t)before + (uint32_t)__builtin_popcount(nib & ((1u << e) - 1u));
-        __builtin_amdgcn_raw_buffer_store_b32(key0 + (uint32_t)e, ro, ((nib >> e) & 1u) ? pos * 4u : 0x80000000u, 0, 0);
+        // this lane's flag of key 4l + e; an unlisted key's offset has bit 31 set (past the end)
+        const uint32_t bit = (uint32_t)(((uint64_t)w[2 * e + 1] << 32 | w[2 * e]) >> lane) & 1u;
+        __builtin_amdgcn_raw_buffer_store_b32(key0 + (uint32_t)e, ro, (pos << 2) | ((bit ^ 1u) << 31), 0, 0);
+        pos += bit;
       }
     }
     if (tid == 0) counts[unit] = min(kept, cap);

@@ -6,7 +6,7 @@
 
 namespace sattn {
 
-constexpr size_t SCORE_STAGE_BUDGET = 1024ull << 20;  // bytes of fp32 scores staged per pass
+constexpr size_t SCORE_STAGE_BUDGET = 2048ull << 20;  // bytes of fp32 scores staged per pass
 
 int mask_heads_per_pass(int BH, int G, int Nk) {
   const size_t per = (size_t)G * (size_t)score_stride(Nk) * 4;

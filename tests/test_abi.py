@@ -253,7 +253,7 @@ def test_workspace_query(lib):
     assert lib.sattn_mask_workspace_bytes(1, 1, 10, 200000, 128, 64) == 0
     # long video: 549 groups x 70200 keys of fp32 scores per head; the staging is bounded
     ws = lib.sattn_mask_workspace_bytes(1, 24, 70200, 70200, 128, 128)
-    assert 549 * 70200 * 4 <= ws <= 1100 * (1 << 20)
+    assert 549 * 70200 * 4 <= ws <= 2100 * (1 << 20)
 
 
 def test_voxel_permutation_matches_generator(lib):
