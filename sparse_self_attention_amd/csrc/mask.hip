@@ -538,6 +538,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       const uint32_t diff = key_lo ^ key_hi;
       int bits = diff ? 32 - __clz(diff) : 0;
       uint32_t prefix = bits == 32 ? 0u : (key_hi >> bits) << bits;
+      int ties = nc;   // candidates whose key equals the cut (all of them when the band is one key)
       while (bits > 0) {
         const int w = bits > 12 ? 12 : bits;
         const int sh = bits - w, nb = 1 << w;
@@ -552,14 +553,17 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         find_bin(hist, nb, kk, wsum, found);
         prefix |= (uint32_t)found[0] << sh;
         kk = found[1];
+        ties = hist[found[0]];
         bits = sh;
         __syncthreads();
       }
       need = kk;
+      // when every key at the cut is kept they are flagged strict, so only a partial tie uses tie_bits
+      const bool all_ties = ties <= need;
       for (int x = tid; x < nc; x += SEL_THREADS) {
         const uint32_t u = order_key(__uint_as_float(cand_key[x]));
         const int jj = cand_j[x];
-        if (u > prefix) atomicOr(&strict_bits[flag_word(jj)], flag_bit(jj));
+        if (u > prefix || (all_ties && u == prefix)) atomicOr(&strict_bits[flag_word(jj)], flag_bit(jj));
         else if (u == prefix) atomicOr(&tie_bits[flag_word(jj)], flag_bit(jj));
       }
       __syncthreads();
@@ -568,6 +572,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       const int shifts[3] = {20, 8, 0};
       const int widths[3] = {12, 12, 8};
       uint32_t prefix = 0, pmask = 0;
+      int ties = 0;
       kk = topk;
       for (int pass = 0; pass < 3; ++pass) {
         const int sh = shifts[pass], nb = 1 << widths[pass];
@@ -589,17 +594,19 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         prefix |= (uint32_t)found[0] << sh;
         pmask |= (uint32_t)(nb - 1) << sh;
         kk = found[1];
+        ties = hist[found[0]];   // the last pass resolves every bit: the keys equal to the cut
         __syncthreads();
       }
       need = kk;
+      const bool all_ties = ties <= need;
       for (int i = 0; i < rows; ++i) {
         uint32_t u[SEL_KPT];
         keys4(rs, i, tid, Nk, u);
         uint64_t st[SEL_KPT], ti[SEL_KPT];
 #pragma unroll
         for (int e = 0; e < SEL_KPT; ++e) {
-          st[e] = __builtin_amdgcn_ballot_w64(u[e] > prefix);
-          ti[e] = __builtin_amdgcn_ballot_w64(u[e] == prefix && u[e] != 0u);
+          st[e] = __builtin_amdgcn_ballot_w64(u[e] > prefix || (all_ties && u[e] == prefix && u[e] != 0u));
+          ti[e] = __builtin_amdgcn_ballot_w64(!all_ties && u[e] == prefix && u[e] != 0u);
         }
         store_ballots(strict_bits, i * SEL_WAVES + wave, st, lane);
         store_ballots(tie_bits, i * SEL_WAVES + wave, ti, lane);
@@ -687,19 +694,18 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
   __syncthreads();
   int32_t* out = idx + unit * (size_t)cap;
   const int kept = tot_s + min(tot_t, need);
-  if (kept > 0 && tot_t <= need) {
-    // Every key at the cut is kept (the common case): a key is listed iff its strict or tie flag is
-    // set.  Lane l's keys 4l .. 4l+3 of a chunk land at consecutive positions after the chunk's base
-    // and the kept keys of lanes below l.  The stores go through a buffer resource over the list, so
-    // an unlisted key (or a position past cap) takes an offset past the end and is dropped: no branches.
+  if (kept > 0 && tot_t == 0) {
+    // Every key at the cut is kept (the common case: such keys are flagged strict), so a key is listed
+    // iff its strict flag is set.  Lane l's keys 4l .. 4l+3 of a chunk land at consecutive positions
+    // after the chunk's base and the kept keys of lanes below l.  The stores go through a buffer
+    // resource over the list, so an unlisted key (or a position past cap) takes an offset past the end
+    // and is dropped: no branches.
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)cap * 4u);
     for (int i = 0; i < rows; ++i) {
       const int x = i * SEL_WAVES + wave;
       const u32x4 s0 = *(const u32x4*)(strict_bits + 8 * x), s1 = *(const u32x4*)(strict_bits + 8 * x + 4);
-      const u32x4 t0 = *(const u32x4*)(tie_bits + 8 * x), t1 = *(const u32x4*)(tie_bits + 8 * x + 4);
-      const uint32_t w[8] = {s0[0] | t0[0], s0[1] | t0[1], s0[2] | t0[2], s0[3] | t0[3],
-                             s1[0] | t1[0], s1[1] | t1[1], s1[2] | t1[2], s1[3] | t1[3]};
-      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(cnt_s[x] + cnt_t[x]);
+      const uint32_t w[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(cnt_s[x]);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) pos += __builtin_amdgcn_mbcnt_hi(w[2 * e + 1], __builtin_amdgcn_mbcnt_lo(w[2 * e], 0u));
       const uint32_t key0 = (uint32_t)(x * SEL_CHUNK + SEL_KPT * lane);

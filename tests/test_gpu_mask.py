@@ -88,6 +88,9 @@ def test_ties_go_to_lowest_index(sattn):
     kb[0, 0, [10, 2000, 2500]] = inputs.f32_to_bf16_bits((20.0 * qm).astype(np.float32))
     idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=2)
     assert idx[0, 0, 0, :2].tolist() == [10, 2000]
+    # top-3: every key at the cut is kept
+    idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=3)
+    assert cnt[0, 0, 0] == 3 and idx[0, 0, 0, :3].tolist() == [10, 2000, 2500]
 
 
 def test_chunked_window_threshold_density(sattn):
@@ -116,6 +119,9 @@ def test_crowded_cut_bin_uses_global_passes(sattn):
     kb = np.broadcast_to(kb[:, :, :1], (1, 1, Nk, D)).copy()
     idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=20000)
     assert np.all(cnt == 20000) and np.all(idx == np.arange(20000))
+    # every key ties and every key is kept
+    idx, cnt = _gpu_mask(sattn, qb, kb, group, topk=Nk)
+    assert np.all(cnt == Nk) and np.all(idx == np.arange(Nk))
 
 
 def test_maximum_key_count(sattn):
