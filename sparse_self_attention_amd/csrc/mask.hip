@@ -53,14 +53,20 @@ __global__ __launch_bounds__(256) void k_group_mean(const uint16_t* __restrict__
   const int nrows = min(group, Nq - r0);
   const int chunk = threadIdx.x % NC, rl = threadIdx.x / NC;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const uint16_t* base = q + (bh * Nq + r0) * D + chunk * 8;
-  for (int r = rl; r < nrows; r += RL) {
-    const u32x4 w = *(const u32x4*)(base + (size_t)r * D);
+  // the group's rows through a buffer resource (rows past the group read zeros), eight loads in flight
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (bh * Nq + r0) * D, (uint32_t)nrows * D * 2u);
+  constexpr int BATCH = 8;
+  for (int rb = rl; rb < nrows; rb += BATCH * RL) {
+    u32x4 w[BATCH];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += bf16_bits_to_float(w[e] & 0xffffu);
-      acc[2 * e + 1] += bf16_bits_to_float(w[e] >> 16);
-    }
+    for (int k = 0; k < BATCH; ++k) w[k] = buffer_load_x4(rq, (uint32_t)((rb + k * RL) * D + chunk * 8) * 2u);
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_bits_to_float(w[k][e] & 0xffffu);
+        acc[2 * e + 1] += bf16_bits_to_float(w[k][e] >> 16);
+      }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rl][chunk * 8 + e] = acc[e];
