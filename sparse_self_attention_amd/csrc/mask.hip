@@ -20,8 +20,8 @@
 //                 radix passes over the staged scores instead.  Threshold: block max + block sum
 //                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Scores are read
 //                 with 16-byte loads, 256 consecutive keys per wave and row.  Keep flags live in LDS
-//                 bitmaps written by wave ballots; the ascending list comes from popcounts, one block
-//                 scan and mbcnt.
+//                 bitmaps written by wave ballots; the ascending list comes from popcounts, block
+//                 scans and mbcnt.
 #include <math.h>
 
 #include <atomic>
@@ -352,8 +352,9 @@ __device__ inline void find_bin_pair(const int* hA, const int* hB, int nb, int k
 //             If the band misses the cut or overflows the LDS list, the cut and the flags are
 //             computed from global memory instead.
 //  threshold: pass 1 max, pass 2 sum of exp, pass 3 marks s >= lse + ln tau in `strict`.
-//  Compaction: popcounts of each chunk's bitmap words, one block scan, then each kept key writes its
-//  index at its rank (mbcnt over the chunk's four ballots); ties are taken lowest index first up to
+//  Compaction: popcounts of each chunk's bitmap words and block scans give each chunk's base; each kept
+//  key writes its index at its rank (mbcnt over the chunk's four ballots).  When every key at the cut is
+//  kept (flagged strict) the loop is branch-free; otherwise ties are taken lowest index first up to
 //  `need`.
 constexpr int SEL_KPT = 4;                          // keys per thread and row (one 16-byte load)
 constexpr int SEL_ROW = SEL_KPT * SEL_THREADS;      // keys per row
