@@ -465,18 +465,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   auto irow = [&]() { return ind_pos(32 * wave + (opaque_lane_id() >> 1)); };
   int kkeys[NKS], vkeys[NVS], ikey = 0, skey = 0;
   const int swave = NW - 1;        // the wave that gathers the keys' E8M0 scales (4-bit product)
+  // The lane's row within a load.  In the variants whose registers overflow (FP8 scores of three waves,
+  // 4-bit scores at D = 64 with three or four waves) it is recomputed from the lane id at each fetch:
+  // held across the loop it is spilled, and its reload right after the gather is issued waits for that
+  // gather (FP8 scores on the voxel workload's 96-row slices: 13.8 -> 8.4 ms).  Elsewhere it stays in a
+  // register (the recompute's scheduling barrier costs 1-4 % there).
+  constexpr bool RECOMPUTE_ROWS = QK4 ? (D == 64 && NW >= 3) : NW == 3;
   auto fetch_keys = [&](int blk) {
+    if constexpr (RECOMPUTE_ROWS) {
+      const int lid = opaque_lane_id();
 #pragma unroll
-    for (int j = 0; j < NKS; ++j) {
-      const int rs = wave + j * NW;
-      const int p = blk * F8_BK + rs * L::RPL + krow_in;
-      if (L::KSETS % NW == 0 || rs < L::KSETS) kkeys[j] = list_at(p);
-    }
+      for (int j = 0; j < NKS; ++j) {
+        const int rs = wave + j * NW;
+        const int p = blk * F8_BK + rs * L::RPL + lid / L::NC;
+        if (L::KSETS % NW == 0 || rs < L::KSETS) kkeys[j] = list_at(p);
+      }
 #pragma unroll
-    for (int j = 0; j < NVS; ++j) {
-      const int rs = wave + j * NW;
-      const int p = blk * F8_BK + rs * L::RPL8 + vrow_in;
-      if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = list_at(p);
+      for (int j = 0; j < NVS; ++j) {
+        const int rs = wave + j * NW;
+        const int p = blk * F8_BK + rs * L::RPL8 + lid / L::NC8;
+        if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = list_at(p);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NKS; ++j) {
+        const int rs = wave + j * NW;
+        const int p = blk * F8_BK + rs * L::RPL + krow_in;
+        if (L::KSETS % NW == 0 || rs < L::KSETS) kkeys[j] = list_at(p);
+      }
+#pragma unroll
+      for (int j = 0; j < NVS; ++j) {
+        const int rs = wave + j * NW;
+        const int p = blk * F8_BK + rs * L::RPL8 + vrow_in;
+        if (L::VSETS % NW == 0 || rs < L::VSETS) vkeys[j] = list_at(p);
+      }
     }
     if (wave < ISETS) {
       const int p = blk * F8_BK + irow();
