@@ -21,9 +21,10 @@
  *    validation mode (SATTN_VALIDATE=1) the device check of the index lists is serialised across
  *    threads (one check word per device); calls that validate wait for each other.
  *  - Environment: SATTN_VALIDATE=1 checks index lists on the device before sattn_forward,
- *    sattn_delta_forward, sattn_fp8_forward and sattn_fp4_forward; SATTN_LOG=1 prints one line per
- *    launch decision (entry point, sizes, kernel variant, workgroups) to stderr; SATTN_SERIAL_GATHER=1
- *    runs sattn_forward, sattn_delta_forward and attn_forward at pipeline depth 1 (every key block's
+ *    sattn_forward_split, sattn_delta_forward, sattn_fp8_forward and sattn_fp4_forward; SATTN_LOG=1
+ *    prints one line per launch decision (entry point, sizes, kernel variant, workgroups) to stderr;
+ *    SATTN_SERIAL_GATHER=1 runs sattn_forward, sattn_forward_split, sattn_delta_forward and
+ *    attn_forward at pipeline depth 1 (every key block's
  *    gather completes before the block before it computes), a slower order whose results must equal
  *    the default double-buffered ones bit for bit (a check for races in the buffering).
  */
@@ -179,6 +180,36 @@ int sattn_forward(const void* q, const void* k, const void* v,
                   const int32_t* idx, const int32_t* counts, int cap,
                   int B, int H, int Nq, int Nk, int D, int group, float scale,
                   void* out, int out_dtype, float* lse, void* stream);
+
+/*
+ * sattn_forward_split_workspace_bytes - device workspace that sattn_forward_split needs: per query
+ * row and part, D fp32 partial outputs and a (max, normaliser) float pair.  0 for invalid sizes.
+ */
+size_t sattn_forward_split_workspace_bytes(int B, int H, int Nq, int D, int splits);
+
+/*
+ * sattn_forward_split - sattn_forward with each group's key list cut into `splits` parts that run
+ * as separate workgroups, then merged.
+ *
+ * The same result as sattn_forward (same definition, inputs, preconditions, out and lse; FG-Attn
+ * review, "What carries the argument"; Chipmunk review, Referee major comment 1), reached for lists
+ * too few or too unequal to fill the GPU in one pass: part p takes whole 32-key blocks
+ * [p n / splits, (p+1) n / splits) of the group's n blocks and leaves its unnormalised output and its
+ * online-softmax state (running max m_p, normaliser l_p) in the workspace; a merge pass forms
+ * out = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p with m = max_p m_p (LongLive DiT blog,
+ * "Online Softmax": the rescale that combines partial softmax states).  The result differs from
+ * sattn_forward's only in fp32 rounding order, within the same error bounds.
+ *   splits: 1 .. 32.
+ *   workspace / ws_bytes: device memory of at least sattn_forward_split_workspace_bytes() bytes,
+ *   16-byte aligned; its contents are overwritten.  Calls sharing a workspace must not overlap.
+ *   Errors as sattn_forward, plus SATTN_ERR_WORKSPACE for a NULL or short workspace and
+ *   SATTN_ERR_ARG for splits outside 1 .. 32.
+ */
+int sattn_forward_split(const void* q, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* counts, int cap,
+                        int B, int H, int Nq, int Nk, int D, int group, float scale, int splits,
+                        void* workspace, size_t ws_bytes,
+                        void* out, int out_dtype, float* lse, void* stream);
 
 /*
  * sattn_delta_forward - Chipmunk sparse-delta step: refresh only the listed keys' part of a

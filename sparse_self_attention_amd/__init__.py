@@ -65,6 +65,10 @@ def _load():
     lib.sattn_mask_noalloc.restype = I
     lib.sattn_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, P]
     lib.sattn_forward.restype = I
+    lib.sattn_forward_split_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.sattn_forward_split_workspace_bytes.restype = Z
+    lib.sattn_forward_split.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P, I, P, P]
+    lib.sattn_forward_split.restype = I
     lib.attn_forward.argtypes = [P, P, P, I, I, I, I, I, F, P, I, P, P]
     lib.attn_forward.restype = I
     lib.sattn_cached_mask.argtypes = [P, P, P, I, I, I, I, I, I, F, F, P, P, I, P]
@@ -238,6 +242,40 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor
                            group, scale, _ptr(out), F32 if out.dtype == torch.float32 else BF16, _ptr(lse),
                            _stream_ptr(q))
     _check("sattn_forward", st)
+    return out, lse
+
+
+def forward_split_workspace_bytes(B: int, H: int, Nq: int, D: int, splits: int) -> int:
+    """Device workspace of sattn_forward_split for these sizes (0 if invalid)."""
+    return int(_load().sattn_forward_split_workspace_bytes(B, H, Nq, D, splits))
+
+
+def forward_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, counts: torch.Tensor,
+                  group: int, splits: int, *, scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  out_dtype: torch.dtype = torch.bfloat16, want_lse: bool = True):
+    """sattn_forward with each group's list in `splits` parts merged at the end (sattn_forward_split).
+    Returns (out, lse or None)."""
+    lib = _load()
+    B, H, Nq, Nk, D = _check_qkv(q, k, v)
+    G = -(-Nq // group)
+    _check_lists(idx, counts, B, H, G, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    _check_out(out, q.shape, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_lse(lse, B, H, Nq, q.device)
+    need = forward_split_workspace_bytes(B, H, Nq, D, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q.device)
+    st = lib.sattn_forward_split(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(counts), idx.shape[-1], B, H, Nq, Nk,
+                                 D, group, scale, int(splits), _ptr(workspace), ws_bytes, _ptr(out),
+                                 F32 if out.dtype == torch.float32 else BF16, _ptr(lse), _stream_ptr(q))
+    _check("sattn_forward_split", st)
     return out, lse
 
 

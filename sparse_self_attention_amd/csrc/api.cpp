@@ -255,6 +255,51 @@ int sattn_forward(const void* q, const void* k, const void* v, const int32_t* id
   return err ? hip_fail(err, fn) : SATTN_OK;
 }
 
+size_t sattn_forward_split_workspace_bytes(int B, int H, int Nq, int D, int splits) {
+  if (B < 1 || H < 1 || Nq < 1 || (D != 64 && D != 128) || splits < 1 || splits > sattn::SPLIT_MAX_PARTS ||
+      (int64_t)B * H * Nq * splits >= I32_MAX)
+    return 0;
+  return sattn::split_workspace_bytes(B, H, Nq, D, splits);
+}
+
+int sattn_forward_split(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* counts,
+                        int cap, int B, int H, int Nq, int Nk, int D, int group, float scale, int splits,
+                        void* workspace, size_t ws_bytes, void* out, int out_dtype, float* lse, void* stream) {
+  static const char* fn = "sattn_forward_split";
+  if (!q || !k || !v || !idx || !counts || !out)
+    return fail(SATTN_ERR_NULL, "%s: q, k, v, idx, counts and out must be non-NULL", fn);
+  if (int r = check_shapes(fn, B, H, Nq, Nk, D)) return r;
+  if (int r = check_group(fn, group)) return r;
+  if (int r = check_scale(fn, scale)) return r;
+  if (cap < 1) return fail(SATTN_ERR_ARG, "%s: cap = %d must be >= 1", fn, cap);
+  if (splits < 1 || splits > sattn::SPLIT_MAX_PARTS)
+    return fail(SATTN_ERR_ARG, "%s: splits = %d must be in 1 .. %d", fn, splits, sattn::SPLIT_MAX_PARTS);
+  if (out_dtype != SATTN_BF16 && out_dtype != SATTN_F32) return fail(SATTN_ERR_ARG, "%s: bad out_dtype", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
+      !aligned(counts, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
+    return fail(SATTN_ERR_ARG, "%s: q, k, v, out, workspace must be 16-byte aligned; idx, counts, lse 4-byte aligned",
+                fn);
+  const int64_t G = (Nq + group - 1) / group;
+  if ((int64_t)B * H * G * splits >= I32_MAX) return fail(SATTN_ERR_SHAPE, "%s: too many groups x splits", fn);
+  const size_t need = sattn_forward_split_workspace_bytes(B, H, Nq, D, splits);
+  if (need == 0) return fail(SATTN_ERR_SHAPE, "%s: too many rows x splits", fn);
+  if (!workspace || ws_bytes < need)
+    return fail(SATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  if (validate_mode()) {
+    int flag = 0;
+    const int err = sattn::validate_index_lists(idx, counts, cap, (int)(B * H * G), Nk, stream, &flag);
+    if (err) return hip_fail(err, fn);
+    if (flag)
+      return fail(SATTN_ERR_INDEX, "%s: index lists invalid (%s%s%s)", fn, (flag & 1) ? "counts out of [0,cap] " : "",
+                  (flag & 2) ? "index out of [0,Nk) " : "", (flag & 4) ? "not strictly ascending" : "");
+  }
+  sattn::FwdArgs a{q, k, v, idx, counts, cap, B, H, Nq, Nk, D, group, scale, out, out_dtype == SATTN_F32, lse,
+                   false, stream};
+  a.serial = serial_gather();
+  const int err = sattn::launch_attn_fwd_split(a, splits, workspace);
+  return err ? hip_fail(err, fn) : SATTN_OK;
+}
+
 int sattn_delta_forward(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* counts,
                         int cap, int B, int H, int Nq, int Nk, int D, int group, float scale, const float* lse,
                         const float* out_prev, float* fresh, void* out, int out_dtype, void* stream) {

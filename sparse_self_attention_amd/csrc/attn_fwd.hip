@@ -74,13 +74,17 @@ constexpr int BKL = 32;
 // DELTA: the Chipmunk sparse-delta update instead of the softmax.  The probabilities use the given
 // (stale) lse instead of a running max and are not renormalised; the epilogue forms
 // out = out_prev - fresh + sum_j p_j v_j and stores the new sum into fresh.
-template <int D, int NW, bool DENSE, bool OUT_F32, bool DELTA>
+// SPLIT: workgroup x covers part x % nsplit of unit x / nsplit's list (its nsplit parts are equal runs of
+// whole key blocks) and stores, per row, the unnormalised fp32 output of its part into out (rows of D
+// floats, part-minor) and the part's running max and normaliser (base 2) as a float pair into lse; the
+// merge kernel below combines the parts.
+template <int D, int NW, bool DENSE, bool OUT_F32, bool DELTA, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_lean(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int cap,
     int Nq, int Nk, int group, int G, float scale_log2, void* __restrict__ out, float* __restrict__ lse,
     uint32_t n_units, const float* __restrict__ lse_in, const float* __restrict__ out_prev,
-    float* __restrict__ fresh, int row0, int serial) {
+    float* __restrict__ fresh, int row0, int serial, int nsplit) {
   using L = FwdLayout<D, BKL>;
   constexpr int NRS = (L::ROWSETS + NW - 1) / NW;
   // The two stages' K and V tiles are separate LDS objects, so the compiler can tell that the reads of
@@ -90,7 +94,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   __shared__ __attribute__((aligned(1024))) char sk1[L::MAT_BYTES];
   __shared__ __attribute__((aligned(1024))) char sv1[L::MAT_BYTES];
 
-  const uint32_t unit = xcd_striped(blockIdx.x, n_units, 128);
+  const uint32_t flat = xcd_striped(blockIdx.x, n_units, 128);
+  const uint32_t unit = SPLIT ? flat / (uint32_t)nsplit : flat;
+  const int part = SPLIT ? (int)(flat % (uint32_t)nsplit) : 0;
   const int g = (int)(unit % (uint32_t)G);
   const uint32_t bh = unit / (uint32_t)G;
   const int lane = threadIdx.x & 63;
@@ -112,10 +118,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     c = counts[bh * (uint32_t)G + g];
     c = c < 0 ? 0 : (c > cap ? cap : c);
   }
+  int lo = 0;   // this part's first list position
+  if (SPLIT) {
+    const int nb_all = (c + BKL - 1) / BKL;
+    const int b0 = (int)((int64_t)part * nb_all / nsplit), b1 = (int)((int64_t)(part + 1) * nb_all / nsplit);
+    lo = b0 * BKL;
+    c = max(min(b1 * BKL, c) - lo, 0);
+  }
   const int nblk = (c + BKL - 1) / BKL;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (size_t)bh * Nk * D, (uint32_t)Nk * L::RB);
-  const int32_t* ilist = DENSE ? nullptr : idx + ((size_t)bh * G + g) * (size_t)cap;
+  const int32_t* ilist = DENSE ? nullptr : idx + ((size_t)bh * G + g) * (size_t)cap + lo;
   // the list through a buffer resource: 32-bit offsets, no 64-bit address arithmetic per load
   const __amdgpu_buffer_rsrc_t ri = make_rsrc(ilist, DENSE ? 0u : (uint32_t)c * 4u);
 
@@ -316,6 +329,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
     return;
   }
   const float l_tot = l_carry + row_sum();
+  if constexpr (SPLIT) {
+    if (row_valid) {
+      const size_t prow = ((size_t)bh * Nq + r0 + wrow) * (size_t)nsplit + part;
+      float* po = (float*)out + prow * D;
+#pragma unroll
+      for (int db = 0; db < L::DBLK; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 32 * db + 8 * i + 4 * hi;
+          *(f32x4*)(po + d0) = f32x4{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+        }
+      if (hi == 0) *(f32x2*)(lse + 2 * prow) = f32x2{m_run, l_tot};
+    }
+    return;
+  }
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_valid) {
     const size_t orow = ((size_t)bh * Nq + r0 + wrow) * D;
@@ -344,15 +372,15 @@ static int launch_lean_t(const FwdArgs& a, int row0) {
              DENSE ? "dense" : "sparse", DELTA ? " delta" : "", a.out_f32 ? "f32" : "bf16", row0, n_units, NW * 64,
              a.serial ? ", pipeline depth 1" : "");
   if (a.out_f32)
-    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, true, DELTA, false>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
-                       a.fresh, row0, a.serial ? 1 : 0);
+                       a.fresh, row0, a.serial ? 1 : 0, 1);
   else
-    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false, DELTA>), dim3(n_units), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attn_fwd_lean<D, NW, DENSE, false, DELTA, false>), dim3(n_units), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx, a.counts, a.cap,
                        a.Nq, a.Nk, a.group, (int)G, scale_log2, a.out, a.lse, n_units, a.lse_in, a.out_prev,
-                       a.fresh, row0, a.serial ? 1 : 0);
+                       a.fresh, row0, a.serial ? 1 : 0, 1);
   return (int)hipGetLastError();
 }
 
@@ -382,6 +410,96 @@ static int launch_fwd_d(const FwdArgs& a) {
 
 int launch_attn_fwd(const FwdArgs& a) {
   return a.D == 64 ? launch_fwd_d<64>(a) : launch_fwd_d<128>(a);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Split lists: each unit's list in nsplit parts, one workgroup per part, then a merge
+// ---------------------------------------------------------------------------------------------
+
+// One wave per query row: out = sum_p w_p O_p / sum_p w_p l_p with w_p = 2^(m_p - max m) (a part with no
+// keys has m_p = -inf and weight 0); lse = (max m + log2 sum_p w_p l_p) ln 2; a row with no keys at all
+// gets out = 0 and lse = -inf, as in the single-pass forward.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void k_split_merge(const float* __restrict__ po, const f32x2* __restrict__ pml,
+                                                     int nsplit, uint32_t rows, void* __restrict__ out,
+                                                     float* __restrict__ lse) {
+  constexpr int E = D / 64;   // dims per lane
+  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const f32x2* ml = pml + (size_t)row * nsplit;
+  float m = -INFINITY;
+  for (int p = 0; p < nsplit; ++p) m = fmaxf(m, ml[p][0]);
+  float l = 0.0f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  if (m > -INFINITY) {
+    for (int p = 0; p < nsplit; ++p) {
+      const f32x2 x = ml[p];
+      if (x[0] == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(x[0] - m);
+      l += w * x[1];
+      const float* o = po + ((size_t)row * nsplit + p) * D + E * lane;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * o[e];
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (OUT_F32) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) ((float*)out)[(size_t)row * D + E * lane + e] = acc[e] * inv;
+  } else {
+    if constexpr (E == 2) {
+      ((uint32_t*)out)[((size_t)row * D + 2 * lane) / 2] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      ((uint16_t*)out)[(size_t)row * D + lane] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.0f) & 0xffffu);
+    }
+  }
+  if (lse != nullptr && lane == 0) lse[row] = l > 0.0f ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int D, int NW>
+static int launch_split_t(const FwdArgs& a, int row0, int nsplit, float* po, float* pml) {
+  const uint32_t G = (uint32_t)((a.Nq + a.group - 1) / a.group);
+  const uint32_t n_parts = (uint32_t)a.B * (uint32_t)a.H * G * (uint32_t)nsplit;
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  log_launch("attn_fwd_lean<D=%d, waves=%d, sparse, split in %d> rows %d.. of each group: %u workgroups x %d threads",
+             D, NW, nsplit, row0, n_parts, NW * 64);
+  hipLaunchKernelGGL((attn_fwd_lean<D, NW, false, false, false, true>), dim3(n_parts), dim3(NW * 64), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.idx,
+                     a.counts, a.cap, a.Nq, a.Nk, a.group, (int)G, scale_log2, (void*)po, pml, n_parts, nullptr,
+                     nullptr, nullptr, row0, a.serial ? 1 : 0, nsplit);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+static int launch_split_d(const FwdArgs& a, int nsplit, void* ws) {
+  const size_t rows = (size_t)a.B * a.H * a.Nq;
+  float* po = (float*)ws;
+  float* pml = (float*)((char*)ws + split_partials_bytes(a.B, a.H, a.Nq, a.D, nsplit));
+  // row slices of at most 128, as in launch_sparse_d
+  const int ns = (a.group + 127) / 128;
+  const int slice = ((a.group + ns - 1) / ns + 31) / 32 * 32;
+  for (int row0 = 0; row0 < a.group; row0 += slice) {
+    const int waves = slice / 32;
+    const int err = waves <= 2 ? launch_split_t<D, 2>(a, row0, nsplit, po, pml)
+                  : waves == 3 ? launch_split_t<D, 3>(a, row0, nsplit, po, pml)
+                               : launch_split_t<D, 4>(a, row0, nsplit, po, pml);
+    if (err) return err;
+  }
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  log_launch("k_split_merge<D=%d>: %zu rows of %d parts, %u workgroups x 256 threads", D, rows, nsplit, grid.x);
+  if (a.out_f32)
+    hipLaunchKernelGGL((k_split_merge<D, true>), grid, dim3(256), 0, (hipStream_t)a.stream, po, (const f32x2*)pml,
+                       nsplit, (uint32_t)rows, a.out, a.lse);
+  else
+    hipLaunchKernelGGL((k_split_merge<D, false>), grid, dim3(256), 0, (hipStream_t)a.stream, po, (const f32x2*)pml,
+                       nsplit, (uint32_t)rows, a.out, a.lse);
+  return (int)hipGetLastError();
+}
+
+int launch_attn_fwd_split(const FwdArgs& a, int nsplit, void* ws) {
+  return a.D == 64 ? launch_split_d<64>(a, nsplit, ws) : launch_split_d<128>(a, nsplit, ws);
 }
 
 }  // namespace sattn

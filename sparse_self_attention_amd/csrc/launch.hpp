@@ -32,6 +32,17 @@ struct FwdArgs {
 };
 int launch_attn_fwd(const FwdArgs& a);
 
+// Split-list forward (sattn_forward_split): workspace = per (row, part) the unnormalised fp32 output
+// (D floats) then, from a 256-byte boundary, the part's running max and normaliser (2 floats).
+inline size_t split_partials_bytes(int B, int H, int Nq, int D, int nsplit) {
+  return ((size_t)B * H * Nq * nsplit * D * 4 + 255) & ~(size_t)255;
+}
+inline size_t split_workspace_bytes(int B, int H, int Nq, int D, int nsplit) {
+  return split_partials_bytes(B, H, Nq, D, nsplit) + (((size_t)B * H * Nq * nsplit * 8 + 255) & ~(size_t)255);
+}
+constexpr int SPLIT_MAX_PARTS = 32;
+int launch_attn_fwd_split(const FwdArgs& a, int nsplit, void* ws);
+
 // Validation of index lists: writes 0 into *flag_host when every list is unique, ascending and in
 // range with 0 <= counts <= cap, else a non-zero code.  Synchronises the stream.
 int validate_index_lists(const int32_t* idx, const int32_t* counts, int cap, int BHG, int Nk, void* stream,

@@ -89,6 +89,13 @@ int main() {
   EXPECT(sattn_forward(P, P, P, I, I, 64, BIG / 2, 4, BIG / 1024, 500, 128, 16, 0.1f, P, SATTN_F32, F, nullptr),
          SATTN_ERR_SHAPE);
   EXPECT(sattn_forward(P, P, nullptr, I, I, 64, 1, 2, 300, 500, 128, 64, 0.1f, P, SATTN_F32, F, nullptr), SATTN_ERR_NULL);
+  const size_t sws = sattn_forward_split_workspace_bytes(1, 2, 300, 128, 3);
+  EXPECT(sattn_forward_split(P, P, P, I, I, 64, 1, 2, 300, 500, 128, 64, 0.1f, 3, P, sws, P, SATTN_F32, F, nullptr),
+         SATTN_ERR_HIP);
+  EXPECT(sattn_forward_split(P, P, P, I, I, 64, 1, 2, 300, 500, 128, 64, 0.1f, 3, P, sws - 1, P, SATTN_F32, F, nullptr),
+         SATTN_ERR_WORKSPACE);
+  EXPECT(sattn_forward_split(P, P, P, I, I, 64, 1, 2, 300, 500, 128, 64, 0.1f, 40, P, sws, P, SATTN_F32, F, nullptr),
+         SATTN_ERR_ARG);
   EXPECT(sattn_delta_forward(P, P, P, I, I, 64, 1, 2, 300, 500, 128, 64, 0.1f, F, F, F, P, SATTN_F32, nullptr), SATTN_ERR_HIP);
   EXPECT(sattn_delta_forward(P, P, P, I, I, 64, 1, 2, 300, 500, 128, 64, 0.1f, F, F, nullptr, P, SATTN_F32, nullptr),
          SATTN_ERR_NULL);

@@ -11,6 +11,7 @@ constexpr int FAKE_HIP_ERROR = 999;
 
 namespace sattn {
 int launch_attn_fwd(const FwdArgs&) { ++g_launches; return FAKE_HIP_ERROR; }
+int launch_attn_fwd_split(const FwdArgs&, int, void*) { ++g_launches; return FAKE_HIP_ERROR; }
 int validate_index_lists(const int32_t*, const int32_t*, int, int, int, void*, int* flag_host) {
   ++g_launches;
   *flag_host = 0;

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"sattn_mask", "sattn_forward", "attn_forward", "sattn_mask_workspace_bytes", "sattn_cached_mask",
             "sattn_colsum_mask", "sattn_delta_forward", "sattn_vsmooth_quantize", "sattn_fp8_forward",
             "sattn_vsmooth_workspace_bytes", "sattn_vsmooth_mean_stride", "sattn_mx4_quantize", "sattn_fp4_forward",
-            "sattn_strerror", "sattn_last_error", "sattn_voxel_permutation", "sattn_permute_tokens"} <= set(names)
+            "sattn_strerror", "sattn_last_error", "sattn_voxel_permutation", "sattn_permute_tokens",
+            "sattn_forward_split", "sattn_forward_split_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sattn.h but not exported"
 
@@ -79,6 +80,33 @@ FWD_CASES = [
 def test_forward_validation(lib, kw, code):
     assert fwd(lib, **kw) == code
     assert lib.sattn_last_error()
+
+
+def fwd_split(lib, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, counts=FAKE, cap=64, B=1, H=1, Nq=128, Nk=128, D=128, group=128,
+              scale=0.1, splits=4, ws=FAKE, ws_bytes=1 << 40, out=FAKE, out_dtype=0, lse=P(0)):
+    return lib.sattn_forward_split(q, k, v, idx, counts, cap, B, H, Nq, Nk, D, group, scale, splits, ws, ws_bytes, out,
+                                   out_dtype, lse, P(0))
+
+
+# sattn_forward's checks plus the split count and the workspace
+SPLIT_CASES = FWD_CASES + [
+    (dict(splits=0), ERR_ARG), (dict(splits=33), ERR_ARG), (dict(ws=P(4104)), ERR_ARG),
+    (dict(ws=P(0)), ERR_WORKSPACE), (dict(ws_bytes=1024), ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,code", SPLIT_CASES, ids=[str(c[0]) for c in SPLIT_CASES])
+def test_forward_split_validation(lib, kw, code):
+    assert fwd_split(lib, **kw) == code
+    assert lib.sattn_last_error()
+
+
+def test_forward_split_workspace_query(lib):
+    # per (row, part): D fp32 partials, then a (max, normaliser) pair; each section 256-byte aligned
+    assert lib.sattn_forward_split_workspace_bytes(1, 12, 7040, 128, 4) == 12 * 7040 * 4 * (128 * 4 + 8)
+    assert lib.sattn_forward_split_workspace_bytes(1, 1, 10, 64, 3) == 7680 + 256
+    for bad in [(0, 1, 10, 64, 2), (1, 1, 10, 96, 2), (1, 1, 10, 64, 0), (1, 1, 10, 64, 33)]:
+        assert lib.sattn_forward_split_workspace_bytes(*bad) == 0
 
 
 MASK_CASES = [
