@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--workload", default="long_70200")
     p.add_argument("--density", type=float, default=None,
                    help="top-k fraction of the keys kept per group instead of the workload's own (a sweep point)")
+    p.add_argument("--splits", type=int, default=1,
+                   help="run each group's key list as this many parts merged afterwards (forward_split; "
+                        "1: the plain forward)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mib", type=int, default=512,
                    help="scratch write between timed steps that flushes the last-level cache (0: none)")
@@ -217,6 +220,9 @@ def main():
             print("--density needs a top-k workload and a fraction in (0, 1]", file=sys.stderr)
             sys.exit(2)
         w = dataclasses.replace(w, keep=args.density)
+    if not 1 <= args.splits <= 32:
+        print("--splits takes 1 to 32 parts per list", file=sys.stderr)
+        sys.exit(2)
     import numpy as np
     import torch
     import sparse_self_attention_amd as sattn
@@ -255,6 +261,10 @@ def main():
     lse = torch.empty((1, w.heads, w.n_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     flush = torch.empty(max(args.flush_mib, 0) << 20, dtype=torch.uint8, device=dev)
+    split_ws = None
+    if args.splits > 1:
+        split_ws = torch.empty(sattn.forward_split_workspace_bytes(1, w.heads, w.n_q, w.dim, args.splits),
+                               dtype=torch.uint8, device=dev)
     # one counts buffer per mask call, so that every step's kept FLOPs are known afterwards
     n_mask_calls = (warm + MASK_EVERY - 1) // MASK_EVERY + (steps + MASK_EVERY - 1) // MASK_EVERY + 1
     counts_of = [torch.empty((1, w.heads, G), dtype=torch.int32, device=dev) for _ in range(n_mask_calls)]
@@ -280,7 +290,11 @@ def main():
             if ev is not None:
                 ev["f0"][s].record(stream)
                 step_counts.append(counts)
-            sattn.forward(qs[i], ks[i], v, idx, counts, w.group, out=out, lse=lse)
+            if split_ws is None:
+                sattn.forward(qs[i], ks[i], v, idx, counts, w.group, out=out, lse=lse)
+            else:
+                sattn.forward_split(qs[i], ks[i], v, idx, counts, w.group, args.splits, workspace=split_ws,
+                                    out=out, lse=lse)
             if ev is not None:
                 ev["f1"][s].record(stream)
         return call
@@ -316,7 +330,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.n_q, "head_dim": w.dim,
                    "group": w.group, "mode": w.mode, "topk": w.topk if w.mode == "topk" else None, "tau": tau,
                    "density": round(kept_pairs / (cnt_h.size * w.n_k), 4), "mask_every": MASK_EVERY,
-                   "grid": list(w.grid_k), "mall_flush_mib": args.flush_mib},
+                   "grid": list(w.grid_k), "mall_flush_mib": args.flush_mib, "splits": args.splits},
         "kept_tflops_fwd": round(fwd_tflops, 2),
         "dense_equiv_tflops_fwd": round(dflops / (fwd_avg * 1e-3) / 1e12, 2),
         "pct_mfma_peak_kept_fwd": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
@@ -326,8 +340,10 @@ def main():
         "gathered_GBps_fwd": round(kept_pairs * 2 * w.dim * 2 / (fwd_avg * 1e-3) / 1e9, 1),
     }
     # dominant kernel: the sparse forward (one launch per step)
-    traffic = recorded_traffic(w.name)
-    rec["roofline"] = {"bound": "mfma", "kernel": f"attn_fwd_lean<{w.dim},sparse,bf16>",
+    traffic = recorded_traffic(w.name) if args.splits == 1 else None
+    kname = f"attn_fwd_lean<{w.dim},sparse,bf16>" if args.splits == 1 else \
+        f"attn_fwd_lean<{w.dim},split,f32> + k_split_merge ({args.splits} parts)"
+    rec["roofline"] = {"bound": "mfma", "kernel": kname,
                        "achieved": round(fwd_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                        "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
     # the gather path beyond L2: the recorded per-launch fetch+write bytes over this run's launch time

@@ -22,6 +22,14 @@ def test_density_needs_a_fraction_and_a_topk_workload():
         assert "--density needs" in r.stderr
 
 
+def test_splits_outside_one_to_32_are_refused():
+    for n in ("0", "33"):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "1", "--warmup", "0",
+                            "--splits", n], capture_output=True, text=True, timeout=300, cwd=ROOT)
+        assert r.returncode == 2, (n, r.stderr[-300:])
+        assert "--splits takes" in r.stderr
+
+
 def test_cpu_baseline_leg_on_the_host():
     """The oracle-timing leg on a tiny workload with the oracle's own lists: a positive kept-FLOP rate, the
     sample described, and the partial tail group always in it (units given only their listed rows)."""
