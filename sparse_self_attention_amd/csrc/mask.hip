@@ -19,9 +19,9 @@
 //                 key index).  If the band misses the cut or overflows LDS, the cut is found by
 //                 radix passes over the staged scores instead.  Threshold: block max + block sum
 //                 of exp, cut = lse + ln(tau), the arg-max key if nothing passes.  Scores are read
-//                 with 16-byte loads, 256 consecutive keys per wave and row.  Keep flags live in LDS
-//                 bitmaps written by wave ballots; the ascending list comes from popcounts, block
-//                 scans and mbcnt.
+//                 with 4-byte loads, 256 consecutive keys per wave and row, 64 per load.  Keep flags
+//                 live in plain LDS bitmaps (bit j % 32 of word j / 32) written by wave ballots; the
+//                 ascending list comes from popcounts, block scans and mbcnt.
 #include <math.h>
 
 #include <atomic>
@@ -341,11 +341,11 @@ __device__ inline void find_bin_pair(const int* hA, const int* hB, int nb, int k
   __syncthreads();
 }
 
-// One 1024-thread workgroup per group.  Keys are visited in rows of SEL_ROW = 4096: thread t reads keys
-// 4t .. 4t+3 of a row with one 16-byte load, so wave w covers the 256 consecutive keys of chunk
-// c = 16 i + w, i.e. keys [256 c, 256 c + 256).  A chunk's flags are its four wave ballots, one per element
-// e of the lanes' loads: bit l of ballot e flags key 256 c + 4 l + e.  Ballot e of chunk c is kept in
-// bitmap words 8c + 2e (lanes 0-31) and 8c + 2e + 1 (lanes 32-63).
+// One 1024-thread workgroup per group.  Keys are visited in rows of SEL_ROW = 4096: wave w covers the 256
+// consecutive keys of chunk c = 16 i + w, i.e. keys [256 c, 256 c + 256), and lane l reads keys
+// 256 c + 64 e + l (e = 0..3, one 4-byte load each, consecutive across the wave).  A chunk's flags are its
+// four wave ballots, one per e: bit l of ballot e flags key 256 c + 64 e + l, so the flag bitmaps are plain
+// (bit j % 32 of word j / 32 flags key j) and ballot e of chunk c is words 8c + 2e and 8c + 2e + 1.
 //  top-k:     the sample locates a band [key_lo, key_hi] around the cut; one pass (global) marks the
 //             keys above it in `strict` and copies the band's keys to LDS; an exact radix select on
 //             them resolves the cut; candidates above it join `strict`, ties at the cut go to `tie`.
@@ -356,10 +356,10 @@ __device__ inline void find_bin_pair(const int* hA, const int* hB, int nb, int k
 //  key writes its index at its rank (mbcnt over the chunk's four ballots).  When every key at the cut is
 //  kept (flagged strict) the loop is branch-free; otherwise ties are taken lowest index first up to
 //  `need`.
-constexpr int SEL_KPT = 4;                          // keys per thread and row (one 16-byte load)
+constexpr int SEL_KPT = 4;                          // keys per thread and row (4-byte loads 64 keys apart)
 constexpr int SEL_ROW = SEL_KPT * SEL_THREADS;      // keys per row
 constexpr int SEL_CHUNK = SEL_KPT * 64;             // keys per (row, wave)
-constexpr int SEL_BATCH = 8;                        // rows (16-byte loads) in flight per thread
+constexpr int SEL_BATCH = 8;                        // rows (four loads each) in flight per thread
 
 static inline size_t select_lds_bytes(int Nk, bool topk) {
   const size_t rows = (size_t)(Nk + SEL_ROW - 1) / SEL_ROW;
@@ -367,20 +367,27 @@ static inline size_t select_lds_bytes(int Nk, bool topk) {
   return 4 * ((topk ? 4096 : 0) + 2 * 8 * chunks + 2 * chunks + (topk ? 2 * SEL_CAND : 0));
 }
 
-// Order keys of keys i*SEL_ROW + 4*tid + e, e = 0..3 (0 past Nk).  The score row is read through a
-// buffer resource (loads past its end return zeros), so the load carries no branch and a batch of them
-// is in flight at once; score rows are padded to a multiple of 32 floats, so a partly valid quad stays
-// inside its row.
+// Key e (0..3) of thread tid in row i: 256 (16 i + wave) + 64 e + lane.
+__device__ inline int sel_key(int i, int tid, int e) { return i * SEL_ROW + (tid >> 6) * SEL_CHUNK + 64 * e + (tid & 63); }
+
+// Score of key e of thread tid in row i (raw bits).  The score row is read through a buffer resource
+// (loads past its end return zeros), so the load carries no branch and a batch of them is in flight at once.
+__device__ inline uint32_t score_bits(__amdgpu_buffer_rsrc_t rs, int i, int tid, int e) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)sel_key(i, tid, e) * 4u, 0, 0);
+}
+
+// Order keys of the four keys of thread tid in row i (0 past Nk).
 __device__ inline void keys4(__amdgpu_buffer_rsrc_t rs, int i, int tid, int Nk, uint32_t (&u)[SEL_KPT]) {
-  const int j = i * SEL_ROW + SEL_KPT * tid;
-  const f32x4 s = __builtin_bit_cast(f32x4, buffer_load_x4(rs, (uint32_t)j * 4u));
+  uint32_t raw[SEL_KPT];
 #pragma unroll
-  for (int e = 0; e < SEL_KPT; ++e) u[e] = j + e < Nk ? order_key(s[e]) : 0u;
+  for (int e = 0; e < SEL_KPT; ++e) raw[e] = score_bits(rs, i, tid, e);
+#pragma unroll
+  for (int e = 0; e < SEL_KPT; ++e) u[e] = sel_key(i, tid, e) < Nk ? order_key(__uint_as_float(raw[e])) : 0u;
 }
 
 // Bitmap word and bit of key j.
-__device__ inline int flag_word(int j) { return 8 * (j >> 8) + 2 * (j & 3) + ((j >> 7) & 1); }
-__device__ inline uint32_t flag_bit(int j) { return 1u << ((j >> 2) & 31); }
+__device__ inline int flag_word(int j) { return j >> 5; }
+__device__ inline uint32_t flag_bit(int j) { return 1u << (j & 31); }
 
 __device__ inline int mbcnt64(uint64_t b) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
@@ -492,21 +499,22 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     const float lo_f = key_lo <= 0x007FFFFFu ? -INFINITY : key_to_float(key_lo);
     int above_w = 0;   // keys above the band seen by this wave (uniform)
     for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
-      f32x4 sv[SEL_BATCH];
+      uint32_t sv[SEL_BATCH][SEL_KPT];
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r)
-        sv[r] = __builtin_bit_cast(f32x4, buffer_load_x4(rs, (uint32_t)((i0 + r) * SEL_ROW + SEL_KPT * tid) * 4u));
+#pragma unroll
+        for (int e = 0; e < SEL_KPT; ++e) sv[r][e] = score_bits(rs, i0 + r, tid, e);
 #pragma unroll
       for (int r = 0; r < SEL_BATCH; ++r) {
         const int i = i0 + r;
         if (i < rows) {
           uint64_t ab[SEL_KPT], bc[SEL_KPT];
           int nb = 0;
-          const int j0 = i * SEL_ROW + SEL_KPT * tid;
+          const int j0 = sel_key(i, tid, 0);
 #pragma unroll
           for (int e = 0; e < SEL_KPT; ++e) {
-            const float x = sv[r][e];
-            const bool valid = j0 + e < Nk;
+            const float x = __uint_as_float(sv[r][e]);
+            const bool valid = j0 + 64 * e < Nk;
             ab[e] = __builtin_amdgcn_ballot_w64(valid && x > hi_f);
             bc[e] = __builtin_amdgcn_ballot_w64(valid && x >= lo_f && x <= hi_f);
             nb += (int)__popcll(bc[e]);
@@ -522,8 +530,8 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
               if ((bc[e] >> lane) & 1u) {
                 const int pos = base + mbcnt64(bc[e]);
                 if (pos < SEL_CAND) {
-                  cand_key[pos] = __float_as_uint(sv[r][e]);
-                  cand_j[pos] = j0 + e;
+                  cand_key[pos] = sv[r][e];
+                  cand_j[pos] = j0 + 64 * e;
                 }
               }
               base += (int)__popcll(bc[e]);
@@ -713,15 +721,17 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       const u32x4 s0 = *(const u32x4*)(strict_bits + 8 * x), s1 = *(const u32x4*)(strict_bits + 8 * x + 4);
       const uint32_t w[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
       uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(cnt_s[x]);
-#pragma unroll
-      for (int e = 0; e < SEL_KPT; ++e) pos += __builtin_amdgcn_mbcnt_hi(w[2 * e + 1], __builtin_amdgcn_mbcnt_lo(w[2 * e], 0u));
-      const uint32_t key0 = (uint32_t)(x * SEL_CHUNK + SEL_KPT * lane);
+      const uint32_t key0 = (uint32_t)(x * SEL_CHUNK + lane);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) {
-        // this lane's flag of key 4l + e; an unlisted key's offset has bit 31 set (past the end)
-        const uint32_t bit = (uint32_t)(((uint64_t)w[2 * e + 1] << 32 | w[2 * e]) >> lane) & 1u;
-        __builtin_amdgcn_raw_buffer_store_b32(key0 + (uint32_t)e, ro, (pos << 2) | ((bit ^ 1u) << 31), 0, 0);
-        pos += bit;
+        // key 256 x + 64 e + l goes after the chunk's kept keys of ballots below e and of lanes below l in
+        // ballot e, so the kept keys of one ballot are stored as one contiguous run; an unlisted key's
+        // offset has bit 31 set (past the end)
+        const uint64_t b = (uint64_t)w[2 * e + 1] << 32 | w[2 * e];
+        const uint32_t bit = (uint32_t)(b >> lane) & 1u;
+        const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi(w[2 * e + 1], __builtin_amdgcn_mbcnt_lo(w[2 * e], 0u));
+        __builtin_amdgcn_raw_buffer_store_b32(key0 + 64u * (uint32_t)e, ro, (p << 2) | ((bit ^ 1u) << 31), 0, 0);
+        pos += (uint32_t)__popcll(b);
       }
     }
     if (tid == 0) counts[unit] = min(kept, cap);
@@ -735,20 +745,16 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
         bs[e] = (uint64_t)strict_bits[8 * x + 2 * e] | ((uint64_t)strict_bits[8 * x + 2 * e + 1] << 32);
         bt[e] = (uint64_t)tie_bits[8 * x + 2 * e] | ((uint64_t)tie_bits[8 * x + 2 * e + 1] << 32);
       }
-      // keys of the chunk before this lane's first key, then this lane's four keys in order
+      // keys of the chunk before key 256 x + 64 e + l: those of ballots below e, then of lanes below l
       int before_s = __builtin_amdgcn_readfirstlane(cnt_s[x]), before_t = __builtin_amdgcn_readfirstlane(cnt_t[x]);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e) {
-        before_s += mbcnt64(bs[e]);
-        before_t += mbcnt64(bt[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < SEL_KPT; ++e) {
         const int st = (int)((bs[e] >> lane) & 1u), tie = (int)((bt[e] >> lane) & 1u);
-        const int pos = before_s + min(before_t, need);
-        if ((st || (tie && before_t < need)) && pos < cap) out[pos] = x * SEL_CHUNK + SEL_KPT * lane + e;
-        before_s += st;
-        before_t += tie;
+        const int ps = before_s + mbcnt64(bs[e]), pt = before_t + mbcnt64(bt[e]);
+        const int pos = ps + min(pt, need);
+        if ((st || (tie && pt < need)) && pos < cap) out[pos] = x * SEL_CHUNK + 64 * e + lane;
+        before_s += (int)__popcll(bs[e]);
+        before_t += (int)__popcll(bt[e]);
       }
     }
     if (tid == 0) counts[unit] = min(kept, cap);
@@ -776,7 +782,7 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
       keys4(rs, i, tid, Nk, u);
 #pragma unroll
       for (int e = 0; e < SEL_KPT; ++e)
-        if (u[e] == bmax && u[e] != 0u) jmin = min(jmin, i * SEL_ROW + SEL_KPT * tid + e);
+        if (u[e] == bmax && u[e] != 0u) jmin = min(jmin, sel_key(i, tid, e));
     }
     jmin = block_min_int(jmin, ired);
     if (tid == 0) {
