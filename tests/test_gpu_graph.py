@@ -66,6 +66,60 @@ def test_graph_replays_match_eager(sattn):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
 
 
+def test_threshold_mask_and_split_forward_graph_replays_match_eager(sattn):
+    """A threshold mask (uneven lists) followed by the split-list forward in three parts, captured into one
+    graph: every replay reproduces the eager lists, output and lse bit for bit."""
+    rng = np.random.default_rng(23)
+    B, H, D, group, Nq, Nk, splits = 1, 2, 128, 128, 900, 4000, 3
+    bits = lambda shape, std: inputs.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+    q = to_device_bf16(bits((B, H, Nq, D), 2.0), DEV)
+    k = to_device_bf16(bits((B, H, Nk, D), 1.0), DEV)
+    v = to_device_bf16(bits((B, H, Nk, D), 1.0), DEV)
+    G = -(-Nq // group)
+    tau = 0.3 / Nk
+    ws = torch.empty(sattn.mask_workspace_bytes(B, H, Nq, Nk, D, group), dtype=torch.uint8, device=DEV)
+    sws = torch.empty(sattn.forward_split_workspace_bytes(B, H, Nq, D, splits), dtype=torch.uint8, device=DEV)
+
+    def buffers():
+        return (torch.empty((B, H, G, Nk), dtype=torch.int32, device=DEV),
+                torch.empty((B, H, G), dtype=torch.int32, device=DEV),
+                torch.empty((B, H, Nq, D), dtype=torch.bfloat16, device=DEV),
+                torch.empty((B, H, Nq), dtype=torch.float32, device=DEV))
+
+    def step(idx, cnt, out, lse):
+        sattn.mask(q, k, group, thresh=tau, idx=idx, counts=cnt, workspace=ws)
+        sattn.forward_split(q, k, v, idx, cnt, group, splits, workspace=sws, out=out, lse=lse)
+
+    ref = buffers()
+    step(*ref)
+    torch.cuda.synchronize()
+    c = ref[1].cpu().numpy()
+    assert c.min() < c.max(), "the threshold lists should differ in length"
+    got = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(*got)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(*got)
+    for rep in range(3):
+        got[0].fill_(-7)
+        got[2].zero_()
+        got[3].fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a_, b_ in (("counts", got[1], ref[1]), ("out", got[2], ref[2]), ("lse", got[3], ref[3])):
+            assert torch.equal(a_, b_), f"replay {rep}: {name} differs from the eager run"
+        for h in range(H):
+            for gi in range(G):
+                n = int(ref[1][0, h, gi])
+                assert torch.equal(got[0][0, h, gi, :n], ref[0][0, h, gi, :n]), f"replay {rep}: list ({h}, {gi})"
+
+
 def test_lowbit_paths_graph_replays_match_eager(sattn):
     """V-Smooth quantisation + FP8 forward, and MXFP4 quantisation of Q and K + FP4-score forward, captured
     together into one graph: every replay reproduces the eager results bit for bit."""

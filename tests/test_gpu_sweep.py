@@ -4,7 +4,7 @@ uniformly over several groups and tiles, queries of standard deviation 1, 2 or 4
 Each path against the fp64 oracle, on inputs the oracle made or seeded lists, never on a GPU result:
 the mask (sets) and the sparse forward on the oracle's lists; the dense path; the cached slice mask and
 the column-sum lists with the oracle's lse; the sparse-delta step; the FP8 value path and the 4-bit
-score path on the oracle's quantisation."""
+score path on the oracle's quantisation; the split-list forward on the oracle's lists."""
 import os
 
 import numpy as np
@@ -89,6 +89,9 @@ FP8_CASES = _draw_list(np.random.default_rng(7004), 12, lambda rng, D, g, nq, nk
     int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
 FP4_CASES = _draw_list(np.random.default_rng(7005), 12, lambda rng, D, g, nq, nk: (
     int(rng.integers(1, min(nk, 1500) + 1)), STD(rng)))
+SPLIT_CASES = _draw_list(np.random.default_rng(7006), 12, lambda rng, D, g, nq, nk: (
+    ("topk", int(rng.integers(1, nk + 1))) if rng.random() < 0.5 else ("thresh", float(10.0 ** rng.uniform(-5.0, -0.3))),
+    int(rng.integers(1, 33)), STD(rng)))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-D{c[1]}-M{c[2]}-{c[3]}x{c[4]}-{c[5]}" for c in CASES])
@@ -212,3 +215,23 @@ def test_fp4_forward(sattn, case):
     i, D, group, Nq, Nk, cmax, q_std = case
     print(f"fp4 sweep case {case}", flush=True)
     run_fp4(sattn, np.random.default_rng(6000 + i), D, group, Nq, Nk, cmax, "random", q_std=q_std)
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=_ids(SPLIT_CASES))
+def test_split_forward(sattn, case):
+    i, D, group, Nq, Nk, (mode, param), splits, q_std = case
+    print(f"split sweep case {case}", flush=True)
+    rng = np.random.default_rng(6000 + i)
+    qb = _bits(rng, (1, 2, Nq, D), q_std)
+    kb, vb = _bits(rng, (1, 2, Nk, D)), _bits(rng, (1, 2, Nk, D))
+    kw = {"topk": param} if mode == "topk" else {"thresh": param}
+    ref = oracle.mask_ref(f64(qb), f64(kb), group, mode, **kw)
+    ridx = np.ascontiguousarray(np.maximum(ref["idx"], 0).astype(np.int32))
+    rcnt = np.ascontiguousarray(ref["counts"].astype(np.int32))
+    q, k, v = (to_device_bf16(x, DEV) for x in (qb, kb, vb))
+    out, lse = sattn.forward_split(q, k, v, torch.from_numpy(ridx).to(DEV), torch.from_numpy(rcnt).to(DEV), group,
+                                   splits, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attention_ref(f64(qb), f64(kb), f64(vb), ridx, rcnt, group, scale_of(D))
+    check_out(out.cpu().numpy(), ro, f"split sweep {i} ({splits} parts)")
+    check_lse(lse.cpu().numpy(), rl, f"split sweep {i} ({splits} parts)")
