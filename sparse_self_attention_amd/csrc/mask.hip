@@ -498,14 +498,21 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
     const float hi_f = key_hi >= 0xFF800000u ? INFINITY : key_to_float(key_hi);
     const float lo_f = key_lo <= 0x007FFFFFu ? -INFINITY : key_to_float(key_lo);
     int above_w = 0;   // keys above the band seen by this wave (uniform)
-    for (int i0 = 0; i0 < rows; i0 += SEL_BATCH) {
-      uint32_t sv[SEL_BATCH][SEL_KPT];
+    // Rows go through two buffers of SEL_BATCH / 2 rows: the next buffer's loads are in flight while the
+    // current one is sorted, so a workgroup waits about one memory latency for the whole pass.
+    constexpr int PB = SEL_BATCH / 2;
+    uint32_t sa[PB][SEL_KPT], sb[PB][SEL_KPT];
+    auto load_rows = [&](uint32_t (&dst)[PB][SEL_KPT], int i0) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r)
+      for (int r = 0; r < PB; ++r)
 #pragma unroll
-        for (int e = 0; e < SEL_KPT; ++e) sv[r][e] = score_bits(rs, i0 + r, tid, e);
+        for (int e = 0; e < SEL_KPT; ++e) dst[r][e] = score_bits(rs, i0 + r, tid, e);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto sort_rows = [&](const uint32_t (&sv)[PB][SEL_KPT], int i0) {
 #pragma unroll
-      for (int r = 0; r < SEL_BATCH; ++r) {
+      for (int r = 0; r < PB; ++r) {
         const int i = i0 + r;
         if (i < rows) {
           uint64_t ab[SEL_KPT], bc[SEL_KPT];
@@ -539,6 +546,16 @@ void k_select(const float* __restrict__ scores, const float* __restrict__ sample
           }
         }
       }
+    };
+    // The loads are unconditional (rows past the end read beyond the buffer resource: zeros, no memory
+    // access), so every path reaches a buffer's first use with the same loads outstanding and the waits
+    // cover only that buffer.
+    load_rows(sa, 0);
+    for (int i0 = 0; i0 < rows; i0 += 2 * PB) {
+      load_rows(sb, i0 + PB);
+      sort_rows(sa, i0);
+      load_rows(sa, i0 + 2 * PB);
+      sort_rows(sb, i0 + PB);
     }
     if (lane == 0) ired[wave] = above_w;
     __syncthreads();
