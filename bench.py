@@ -436,11 +436,16 @@ def main():
         dout = torch.empty_like(out_prev)
         d_ms = timed(lambda: sattn.delta_forward(qs[-1], ks[-1], v, idx, counts, w.group, lse=lse, out_prev=out_prev,
                                                  fresh=fresh, out=dout))
+        # kept FLOPs of the column-sum lists the delta step ran on
         rec["chipmunk_delta"] = {"colsum_mask_ms": round(cs_ms, 3), "delta_fwd_ms": round(d_ms, 3),
-                                 "delta_kept_tflops": round(kflops / (d_ms * 1e-3) / 1e12, 2)}
+                                 "delta_kept_tflops": round(kept_flops(counts.cpu().numpy(), w) / (d_ms * 1e-3) / 1e12, 2)}
         del out_prev, fresh, dout
-        # FP8 value path on the same step and lists: V-Smooth quantisation of V, then the forward with
-        # ExpCast bytes and the E4M3 P.V product; its distance from the bf16 path's output
+        # FP8 value path on the step-0 pooled lists (the lists the bf16 forward of the timed steps uses;
+        # the column-sum step above overwrote the buffers): V-Smooth quantisation of V, then the forward
+        # with ExpCast bytes and the E4M3 P.V product, its time against the bf16 forward on the same lists
+        # and its distance from the bf16 path's output
+        sattn.mask(q0, k0, w.group, idx=idx, counts=counts, workspace=ws, **mask_kw)
+        kflops = kept_flops(counts.cpu().numpy(), w)
         vws = torch.empty(sattn.vsmooth_workspace_bytes(1, w.heads, w.n_k, w.dim), dtype=torch.uint8, device=dev)
         codes, vscale, vmean = sattn.vsmooth_quantize(v, workspace=vws)
         q8_ms = timed(lambda: sattn.vsmooth_quantize(v, codes=codes, vscale=vscale, vmean=vmean, workspace=vws))
