@@ -103,8 +103,9 @@ def mx4_dequantize_ref(codes, exps) -> np.ndarray:
 
 
 def fp4_attention_ref(q_codes, q_exps, k_codes, k_exps, v_codes, vscale, vmean, idx, counts, group: int,
-                      scale: float):
+                      scale: float, tie_rel: float = 0.0):
     """The FP8 value path with scores from the dequantised FP4 queries and keys: the block-scaled
-    product of the blog is the exact dot product of the dequantised vectors."""
+    product of the blog is the exact dot product of the dequantised vectors.  tie_rel: as in
+    fp8_attention_ref (then also the per-row slacks and loose rows)."""
     return fp8_attention_ref(mx4_dequantize_ref(q_codes, q_exps), mx4_dequantize_ref(k_codes, k_exps), v_codes,
-                             vscale, vmean, idx, counts, group, scale)
+                             vscale, vmean, idx, counts, group, scale, tie_rel=tie_rel)

@@ -141,7 +141,8 @@ def dequantize_ref(codes, scale, mean) -> np.ndarray:
     return _DEC[codes] * scale[:, :, None, :] + mean[:, :, np.arange(N) // VS_BLOCK, :]
 
 
-def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale: float, block: int = FP8_BLOCK):
+def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale: float, block: int = FP8_BLOCK,
+                      tie_rel: float = 0.0):
     """out, lse of the FP8 value path over per-group key lists.
 
     For each group and its listed keys J (list order), blocks of `block` keys: s2 = scale q.k log2 e
@@ -150,6 +151,21 @@ def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale
     gathered earlier are scaled by 2^(m_old - m_new); O += decode(P) @ Vhat[J], l += sum decode(P), with
     Vhat = scale * E4M3(code) + block mean.  out = O / l; lse = ln(l) + (m - 8) ln 2.
     c = 0 gives out = 0, lse = -inf.
+
+    Rounding ties.  The bytes and the first reference point are integer decisions on the scores.  A
+    computation whose scores carry an error up to tie_rel * scale * log2 e * sum_d |q_d k_d| (for example
+    fp32 dot products: tie_rel = (D + 2) 2^-24) may take a decision whose value lies that close to its
+    boundary the other way; both results are ExpCast results of the same scores, one code apart in that
+    byte (V-Smart/ExpCast summary, third paragraph).  With tie_rel > 0 the function also returns, per
+    query row: out_slack, a bound on max_d |out' - out| over every such choice of the byte decisions
+    (a byte rounded to the other neighbour changes its weight by dp_j, the difference of the two decoded
+    codes, a byte of 127 standing for a move of the reference point: twice the code 8 below; then
+    out' - out = sum_j e_j (Vhat_j - out) / (l + sum_j e_j) with |e_j| <= dp_j), as
+    max_d sum_j dp_j |Vhat_jd - out_d| / (l - sum_j dp_j), all weights in the row's final frame;
+    lse_slack = -ln(1 - sum_j dp_j / l); and loose, the rows whose first reference point ceil(8 max) is
+    such a decision (the neighbouring phase moves every byte by one code, which no per-key bound covers).
+    A move by one more whole log2 unit than needed rescales exactly and changes nothing but weights
+    below the subnormal range, so it is not counted.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -160,6 +176,10 @@ def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale
     Dv = vhat.shape[-1]
     out = np.zeros((B, H, Nq, Dv))
     lse = np.full((B, H, Nq), -np.inf)
+    ties = tie_rel > 0.0
+    out_slack = np.zeros((B, H, Nq))
+    lse_slack = np.zeros((B, H, Nq))
+    loose = np.zeros((B, H, Nq), dtype=bool)
     for b in range(B):
         for h in range(H):
             for g in range(G):
@@ -173,11 +193,19 @@ def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale
                 m8 = np.zeros(rows)
                 o = np.zeros((rows, Dv))
                 l = np.zeros(rows)
+                if ties:
+                    # half-width of the uncertain window of each byte's pre-rounding value 8 (s2 - m) + 120
+                    win = 8.0 * tie_rel * scale * log2e * np.matmul(np.abs(q[b, h, r0:r1]), np.abs(k[b, h, J]).T)
+                    near_ties = []                                      # (row, list position, dp, m8 then)
                 for j0 in range(0, c, block):
                     sb = s2[:, j0:j0 + block]
                     bm = sb.max(axis=1)
                     if j0 == 0:
                         m8 = np.ceil(8.0 * bm)
+                        if ties:
+                            wmax = win[np.arange(rows), sb.argmax(axis=1)]
+                            x8 = 8.0 * bm
+                            loose[b, h, r0:r1] = (np.ceil(x8) - x8 < wmax) | (x8 - np.floor(x8) < wmax)
                     else:
                         move = bm > m8 / 8.0 + RESCALE_SLACK
                         m8new = np.where(move, m8 + 8.0 * np.ceil(bm - m8 / 8.0), m8)
@@ -185,9 +213,31 @@ def fp8_attention_ref(q, k, codes, vscale, vmean, idx, counts, group: int, scale
                         o *= alpha[:, None]
                         l *= alpha
                         m8 = m8new
-                    p = _DEC[expcast_byte(sb - m8[:, None] / 8.0)]
+                    byte = expcast_byte(sb - m8[:, None] / 8.0)
+                    p = _DEC[byte]
                     o += p @ vhat[b, h, J[j0:j0 + block]]
                     l += p.sum(axis=1)
+                    if ties:
+                        y = sb * 8.0 - m8[:, None] + EXPCAST_BIAS
+                        near = np.abs(y - np.floor(y) - 0.5) < win[:, j0:j0 + block]
+                        other = np.where(np.rint(y) == np.floor(y), np.floor(y) + 1.0, np.floor(y))
+                        other = np.clip(other, 0.0, 127.0).astype(np.int64)
+                        p_other = np.where(other == 127, 2.0 * _DEC[119], _DEC[np.minimum(other, 126)])
+                        dp = np.where(near, np.abs(p_other - p), 0.0)
+                        for rr, jj in zip(*np.nonzero(dp)):
+                            near_ties.append((rr, j0 + jj, dp[rr, jj], m8[rr]))
                 out[b, h, r0:r1] = o / l[:, None]
                 lse[b, h, r0:r1] = (np.log2(l) + m8 / 8.0 - 8.0) / log2e
+                if ties:
+                    dsum = np.zeros(rows)
+                    dvec = np.zeros((rows, Dv))
+                    for rr, jj, d, m8_then in near_ties:
+                        d *= np.exp2((m8_then - m8[rr]) / 8.0)          # into the row's final frame
+                        dsum[rr] += d
+                        dvec[rr] += d * np.abs(vhat[b, h, J[jj]] - out[b, h, r0 + rr])
+                    frac = np.minimum(dsum / l, 0.999)
+                    out_slack[b, h, r0:r1] = dvec.max(axis=1) / (l * (1.0 - frac))
+                    lse_slack[b, h, r0:r1] = -np.log1p(-frac)
+    if ties:
+        return out, lse, out_slack, lse_slack, loose
     return out, lse

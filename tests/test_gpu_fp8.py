@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (EXPCAST_TV, check_expcast_bound, check_lse, check_out_fp8, f64, onehot_case,
+from gpu_util import (EXPCAST_TV, check_expcast_bound, check_fp8_path, check_lse, f64, fp8_tie_rel, onehot_case,
                       onehot_total_variation, oracle_vsmooth_head, scale_of, structured_lists, to_device_bf16,
                       value_ranges, vsmooth_to_device, workload)
 from synth import inputs
@@ -84,16 +84,16 @@ def _run_case(sattn, rng, D, group, Nq, Nk, cmax, kind, q_std=1.0, zero_group=Tr
     idx = structured_lists(rng, B, H, G, Nk, counts, kind)
     rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
     scale = scale_of(D)
-    ro, rl = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale)
+    ref = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale, tie_rel=fp8_tie_rel(D))
     codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
     q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
     ti, tc = torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV)
     out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, ti, tc, group, out_dtype=torch.float32)
     torch.cuda.synchronize()
     what = f"D={D} group={group} Nq={Nq} Nk={Nk} c<={cmax} {kind}"
-    check_out_fp8(out.cpu().numpy(), ro, rm, what)
-    check_lse(lse.cpu().numpy(), rl, what)
-    # the exact restricted softmax over the same dequantised values, to the summary's ExpCast bound
+    check_fp8_path(out.cpu().numpy(), lse.cpu().numpy(), ref, rm, what)
+    # the exact restricted softmax over the same dequantised values, to the summary's ExpCast bound (every
+    # row, the rows with a near-tie reference point included)
     vhat = oracle.dequantize_ref(rc, rs, rm)
     eo, el = oracle.sparse_attention_ref(f64(qb), f64(kb), vhat, idx, counts, group, scale)
     check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
@@ -220,6 +220,13 @@ def test_fp8_full_size_sampled(sattn):
         r = slice(g * w.group, min((g + 1) * w.group, w.n_q))
         ui = idx[:, :1, g:g + 1]
         uc = counts[:, :1, g:g + 1]
-        ro, rl = oracle.fp8_attention_ref(f64(qb[:, :1, r]), f64(kb[:, :1]), rc, rs, rm, ui, uc, w.group, scale)
-        check_out_fp8(out_h[:, :1, r], ro, rm, f"long_70200 fp8 g={g}")
-        check_lse(lse_h[:, :1, r], rl, f"long_70200 fp8 g={g}")
+        ref = oracle.fp8_attention_ref(f64(qb[:, :1, r]), f64(kb[:, :1]), rc, rs, rm, ui, uc, w.group, scale,
+                                       tie_rel=fp8_tie_rel(w.dim))
+        loose = check_fp8_path(out_h[:, :1, r], lse_h[:, :1, r], ref, rm, f"long_70200 fp8 g={g}")
+        if loose.any():
+            vhat = oracle.dequantize_ref(rc, rs, rm)
+            eo, el = oracle.sparse_attention_ref(f64(qb[:, :1, r]), f64(kb[:, :1]), vhat, ui, uc, w.group, scale)
+            vr = value_ranges(vhat, ui, uc, w.group, eo.shape[2])
+            check_expcast_bound(out_h[:, :1, r][loose], lse_h[:, :1, r][loose], eo[loose], el[loose], vr[loose],
+                                f"long_70200 fp8 g={g} (near-tie rows) vs exact softmax",
+                                mean_abs_max=float(np.abs(rm).max()))

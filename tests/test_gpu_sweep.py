@@ -11,8 +11,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (MASK_BAND, check_lse, check_mask_sets, check_out, check_out_fp8, check_out_scaled, f64,
-                      scale_of, structured_lists, to_device_bf16, vsmooth_to_device)
+from gpu_util import (MASK_BAND, check_expcast_bound, check_fp8_path, check_lse, check_mask_sets, check_out,
+                      check_out_scaled, f64, fp8_tie_rel, scale_of, structured_lists, to_device_bf16, value_ranges,
+                      vsmooth_to_device)
 from synth import inputs
 from test_gpu_cached import check_cached_sets
 from test_gpu_delta import LOG_BAND, _check_colsum_sets
@@ -200,14 +201,17 @@ def test_fp8_forward(sattn, case):
     counts = rng.integers(1, cmax + 1, size=(B, H, G)).astype(np.int32)
     idx = structured_lists(rng, B, H, G, Nk, counts, "random")
     rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
-    ro, rl = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale_of(D))
+    ref = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale_of(D), tie_rel=fp8_tie_rel(D))
     codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
     q, k = to_device_bf16(qb, DEV), to_device_bf16(kb, DEV)
     out, lse = sattn.fp8_forward(q, k, codes, vscale, vmean, torch.from_numpy(idx).to(DEV),
                                  torch.from_numpy(counts).to(DEV), group, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    check_out_fp8(out.cpu().numpy(), ro, rm, f"fp8 sweep {i}")
-    check_lse(lse.cpu().numpy(), rl, f"fp8 sweep {i}")
+    check_fp8_path(out.cpu().numpy(), lse.cpu().numpy(), ref, rm, f"fp8 sweep {i}")
+    vhat = oracle.dequantize_ref(rc, rs, rm)
+    eo, el = oracle.sparse_attention_ref(f64(qb), f64(kb), vhat, idx, counts, group, scale_of(D))
+    check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
+                        f"fp8 sweep {i} vs exact softmax", mean_abs_max=float(np.abs(rm).max()))
 
 
 @pytest.mark.parametrize("case", FP4_CASES, ids=_ids(FP4_CASES))
