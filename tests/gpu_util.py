@@ -112,7 +112,11 @@ def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str):
 
 
 def check_mask_sets(idx_gpu, cnt_gpu, ref, units, what, exact_counts):
-    """Kept sets may differ from the oracle's only on keys within MASK_BAND of the group's cut."""
+    """Kept sets may differ from the oracle's only on keys within MASK_BAND of the group's cut.  A threshold
+    that no key reaches keeps the arg-max alone (lowest index on ties); scores within MASK_BAND of the
+    maximum are ties up to the rounding of either side (the oracle's fp64 matrix product can round
+    identical key rows differently), so a single key kept by the GPU is valid if its score is that close
+    to the maximum."""
     for (b, h, g) in units:
         c = int(cnt_gpu[b, h, g])
         got = idx_gpu[b, h, g, :c]
@@ -122,7 +126,10 @@ def check_mask_sets(idx_gpu, cnt_gpu, ref, units, what, exact_counts):
             assert c == rc, f"{what} {b, h, g}: count {c} != {rc}"
         diff = set(got.tolist()) ^ set(ref["idx"][b, h, g, :rc].tolist())
         s, t = ref["s"][b, h, g], ref["t"][b, h, g]
-        bad = [j for j in diff if not abs(s[j] - t) <= MASK_BAND]
+        argmax_alone = rc == 1 and s[ref["idx"][b, h, g, 0]] < t     # no key reached the cut
+        smax = s.max()
+        bad = [j for j in diff if not (abs(s[j] - t) <= MASK_BAND
+                                       or (argmax_alone and c == 1 and s[j] >= smax - MASK_BAND))]
         assert not bad, f"{what} {b, h, g}: {len(bad)} keys outside the band, e.g. j={bad[0]} s-t={s[bad[0]] - t:.3g}"
 
 
