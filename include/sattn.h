@@ -286,6 +286,11 @@ int sattn_vsmooth_quantize(const void* v, int B, int H, int Nk, int D, uint8_t* 
  *     lse[i] = ln(sum_j p_j) + (m - 8) ln 2.
  *   q, k, idx, counts, cap, group, scale, out, out_dtype, lse: as sattn_forward (same list
  *   preconditions); codes, vscale, vmean: the outputs of sattn_vsmooth_quantize for V.
+ * Range: the sums are kept in the frame of the row's first reference point, each later block scaled
+ * by 2^(m - m_first) with that factor capped at 2^90 so the fp32 sums stay finite.  A row whose
+ * largest listed score exceeds m_first by more than 90 log2 units (62.38 in units of scale q.k)
+ * weighs its later keys as if the excess were 90 log2 units; no error is reported for it.  Rows
+ * within that range get the result above.
  * Errors: as sattn_forward; codes, vscale and vmean must be 16-byte aligned.
  */
 int sattn_fp8_forward(const void* q, const void* k, const uint8_t* codes, const float* vscale,
@@ -314,7 +319,8 @@ int sattn_mx4_quantize(const void* x, int B, int H, int N, int D, uint8_t* codes
  * sattn_fp4_forward - sattn_fp8_forward with the scores from the MXFP4 queries and keys:
  * s = scale * sum_b 2^(eq_b + ek_b) E2M1(q_b) . E2M1(k_b), on v_mfma_scale_f32_32x32x64_f8f6f4 in
  * FP4 x FP4.  q4, q_scales, k4, k_scales: sattn_mx4_quantize of Q and K; everything else as
- * sattn_fp8_forward.  Errors: as sattn_fp8_forward; q4 and k4 16-byte, the scales 4-byte aligned.
+ * sattn_fp8_forward (its range limit included).  Errors: as sattn_fp8_forward; q4 and k4 16-byte, the
+ * scales 4-byte aligned.
  */
 int sattn_fp4_forward(const uint8_t* q4, const uint8_t* q_scales, const uint8_t* k4, const uint8_t* k_scales,
                       const uint8_t* codes, const float* vscale, const void* vmean,

@@ -58,14 +58,15 @@ def check_fp8_path(o_gpu: np.ndarray, l_gpu: np.ndarray, ref, vmean: np.ndarray,
     bytes of the score; V-Smart/ExpCast summary, third paragraph).  lse bar: the stated one plus the lse
     slack.  Rows whose first reference point is itself such a tie (`loose`: every byte of the row may move
     by one code) are left out here; they must be rare and the caller checks them against the exact
-    restricted softmax (check_expcast_bound); the count allowed (2 + 2 % of the rows) only guards against a
-    window that is far too wide.  rel-L2 is taken over the error beyond the mean-restore and tie terms.
+    restricted softmax (check_expcast_bound); the count allowed (2 + 10 % of the rows; the share grows with
+    the window, i.e. with |scores|: ~4 % at query spreads of 30) only guards against a window that is far
+    too wide.  rel-L2 is taken over the error beyond the mean-restore and tie terms.
     Returns the loose-row mask."""
     out, lse, oslack, lslack, loose = ref
     o_gpu = o_gpu.astype(np.float64)
     l_gpu = l_gpu.astype(np.float64)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
-    assert loose.sum() <= 2 + 0.02 * loose.size, \
+    assert loose.sum() <= 2 + 0.1 * loose.size, \
         f"{what}: {int(loose.sum())} of {loose.size} rows have a near-tie reference point"
     keep = ~loose
     allow = 2.0 ** -8 * float(np.abs(vmean).max(initial=0.0)) + oslack     # per row: the analytic terms

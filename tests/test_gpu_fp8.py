@@ -230,3 +230,37 @@ def test_fp8_full_size_sampled(sattn):
             check_expcast_bound(out_h[:, :1, r][loose], lse_h[:, :1, r][loose], eo[loose], el[loose], vr[loose],
                                 f"long_70200 fp8 g={g} (near-tie rows) vs exact softmax",
                                 mean_abs_max=float(np.abs(rm).max()))
+
+
+def test_fp8_scores_rising_close_to_the_range_limit(sattn):
+    """Later keys score up to ~80 log2 units above the first block's maximum (inside the kernel's 90-unit
+    frame range): large moves of the reference point, the earlier sums scaled down by exact powers of two;
+    the result still matches the oracle and the exact restricted softmax."""
+    rng = np.random.default_rng(90)
+    D, group, Nq, Nk = 64, 32, 32, 512
+    q = np.zeros((1, 1, Nq, D), dtype=np.float32)
+    q[..., 0] = 8.0
+    q[..., 1:] = 0.25 * rng.standard_normal((1, 1, Nq, D - 1))
+    k = rng.standard_normal((1, 1, Nk, D)).astype(np.float32)
+    k[0, 0, 300, 0], k[0, 0, 301, 0], k[0, 0, 420, 0], k[0, 0, 500, 0] = 58.0, 57.5, 56.0, 40.0
+    qb, kb = inputs.f32_to_bf16_bits(q), inputs.f32_to_bf16_bits(k)
+    off = np.repeat(rng.uniform(-2, 2, size=(1, Nk // 128, 1)), 128, axis=1)[None]
+    vb = inputs.f32_to_bf16_bits((rng.standard_normal((1, 1, Nk, D)) + off).astype(np.float32))
+    idx = np.arange(Nk, dtype=np.int32)[None, None, None, :]
+    counts = np.full((1, 1, 1), Nk, dtype=np.int32)
+    scale = scale_of(D)
+    s2 = (f64(qb)[0, 0] @ f64(kb)[0, 0].T) * scale / np.log(2.0)
+    growth = s2.max(axis=1) - np.ceil(8.0 * s2[:, :64].max(axis=1)) / 8.0
+    assert 70.0 < growth.min() and growth.max() < 90.0
+    rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
+    ref = oracle.fp8_attention_ref(f64(qb), f64(kb), rc, rs, rm, idx, counts, group, scale, tie_rel=fp8_tie_rel(D))
+    codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
+    out, lse = sattn.fp8_forward(to_device_bf16(qb, DEV), to_device_bf16(kb, DEV), codes, vscale, vmean,
+                                 torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV), group,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_fp8_path(out.cpu().numpy(), lse.cpu().numpy(), ref, rm, "scores near the range limit")
+    vhat = oracle.dequantize_ref(rc, rs, rm)
+    eo, el = oracle.sparse_attention_ref(f64(qb), f64(kb), vhat, idx, counts, group, scale)
+    check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
+                        "scores near the range limit vs exact softmax", mean_abs_max=float(np.abs(rm).max()))
