@@ -30,8 +30,15 @@ def _bits(rng, shape, std=1.0):
     return inputs.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
 
 
-def _check_colsum_sets(idx, cnt, rows, topk, band, what):
-    """rows: {(b, h, g): oracle column sums}.  Exact counts; sets differ only near the k-th sum."""
+# fp32's smallest normal number: each probability the kernel adds into a column sum underflows below it (to
+# zero or to a few bits), so a sum of a group's M probabilities is lost up to about M times it
+FP32_TINY = 2.0 ** -126
+
+
+def _check_colsum_sets(idx, cnt, rows, topk, band, what, group=1):
+    """rows: {(b, h, g): oracle column sums}.  Exact counts; sets differ only near the k-th sum, or, when
+    the k-th sum lies where fp32 loses such sums (below 4 M 2^-126, M the group size: very peaked rows),
+    among the keys whose sums do too: there they are ties, whatever the oracle's fp64 values."""
     for (b, h, g), c in rows.items():
         n = int(cnt[b, h, g])
         assert n == topk, f"{what} {b, h, g}: count {n} != {topk}"
@@ -40,7 +47,9 @@ def _check_colsum_sets(idx, cnt, rows, topk, band, what):
         order = np.lexsort((np.arange(c.size), -c))
         want = order[:topk]
         t = c[order[topk - 1]]
-        bad = [j for j in set(got.tolist()) ^ set(want.tolist()) if not abs(math.log(c[j]) - math.log(t)) <= band]
+        lost = 4.0 * group * FP32_TINY
+        bad = [j for j in set(got.tolist()) ^ set(want.tolist())
+               if not ((t < lost and c[j] < lost) or (c[j] > 0.0 and abs(math.log(c[j]) - math.log(t)) <= band))]
         assert not bad, f"{what} {b, h, g}: {len(bad)} keys outside the band"
 
 
@@ -62,7 +71,7 @@ def test_colsum_random(sattn, D, group, Nq, Nk, topk):
     torch.cuda.synchronize()
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
     rows = oracle.colsum_scores_ref(q64, k64, group, scale, lse)
-    _check_colsum_sets(idx, cnt, rows, topk, LOG_BAND, f"colsum D={D} M={group}")
+    _check_colsum_sets(idx, cnt, rows, topk, LOG_BAND, f"colsum D={D} M={group}", group)
     if topk == Nk:
         assert np.all(idx == np.arange(Nk))
 
@@ -145,7 +154,7 @@ def test_full_size_sampled(sattn, name):
         lse_rows = oracle.row_lse_ref(qg, kh, scale)
         rows[(0, h, g)] = oracle.colsum_scores_ref(qg, kh, r1 - r0, scale, lse_rows)[(0, 0, 0)]
     # the library's lse is within LSE_ABS of the exact one, which moves a column sum by at most that factor
-    _check_colsum_sets(idx_h, cnt_h, rows, w.topk, LOG_BAND + 2 * LSE_ABS, name)
+    _check_colsum_sets(idx_h, cnt_h, rows, w.topk, LOG_BAND + 2 * LSE_ABS, name, w.group)
     # one delta step over seeded random lists (10 % of keys per group) with a synthetic lse
     G = w.groups
     counts = np.full((1, w.heads, G), w.topk, dtype=np.int32)

@@ -172,7 +172,7 @@ def test_colsum_and_delta(sattn, case):
     idx, cnt = sattn.colsum_mask(q, k, t(lse.astype(np.float32)), group, topk)
     torch.cuda.synchronize()
     rows = oracle.colsum_scores_ref(q64, k64, group, scale, lse)
-    _check_colsum_sets(idx.cpu().numpy(), cnt.cpu().numpy(), rows, topk, LOG_BAND, f"colsum sweep {i}")
+    _check_colsum_sets(idx.cpu().numpy(), cnt.cpu().numpy(), rows, topk, LOG_BAND, f"colsum sweep {i}", group)
     # one delta step over seeded lists (not the GPU's) with the oracle's lse
     counts = rng.integers(0, cap + 1, size=(B, H, G)).astype(np.int32)
     lists = inputs.random_index_lists(rng, B, H, G, Nk, counts, cap)
