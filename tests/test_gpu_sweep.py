@@ -239,3 +239,38 @@ def test_split_forward(sattn, case):
     ro, rl = oracle.sparse_attention_ref(f64(qb), f64(kb), f64(vb), ridx, rcnt, group, scale_of(D))
     check_out(out.cpu().numpy(), ro, f"split sweep {i} ({splits} parts)")
     check_lse(lse.cpu().numpy(), rl, f"split sweep {i} ({splits} parts)")
+
+
+# Cases seeded stress runs found at the edge of the parity checks, kept as regressions: an FP8 byte at a
+# rounding tie on a heavily weighted key (the row's tie slack), FP8 outputs small next to the block means
+# (rel-L2 beyond the mean-restore term), and column sums below fp32's range at the top-k cut (query spreads
+# of 20 and 30).
+STRESS_FP8 = [(88, 64, 96, 712, 1602, 692, 4.0), (27, 128, 96, 36, 1559, 848, 1.0)]
+STRESS_COLSUM = [(5, 128, 96, 1, 3767, 3664, 1519, 20.0), (144, 128, 16, 569, 3581, 3410, 3504, 30.0)]
+
+
+@pytest.mark.parametrize("case", STRESS_FP8, ids=_ids(STRESS_FP8))
+def test_fp8_forward_stress_cases(sattn, case):
+    test_fp8_forward(sattn, case)
+
+
+@pytest.mark.parametrize("case", STRESS_COLSUM, ids=_ids(STRESS_COLSUM))
+def test_colsum_and_delta_stress_cases(sattn, case):
+    test_colsum_and_delta(sattn, case)
+
+
+def test_threshold_argmax_over_identical_keys(sattn):
+    """Every key row identical (every score equal) and a threshold no key reaches: the GPU keeps key 0
+    (arg-max, lowest index); the oracle's fp64 product may round the equal scores apart, and the set check
+    accepts any key within the band of the maximum."""
+    rng = np.random.default_rng(89)
+    D, group, Nq, Nk = 128, 240, 21, 7270
+    qb = _bits(rng, (1, 2, Nq, D))
+    kb = np.broadcast_to(_bits(rng, (1, 1, 1, D)), (1, 2, Nk, D)).copy()
+    tau = 0.0022375465821225056
+    ref = oracle.mask_ref(f64(qb), f64(kb), group, "thresh", thresh=tau)
+    idx, cnt = sattn.mask(to_device_bf16(qb, DEV), to_device_bf16(kb, DEV), group, thresh=tau)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert np.all(cnt == 1) and np.all(idx[..., 0] == 0)
+    check_mask_sets(idx, cnt, ref, [(0, h, 0) for h in range(2)], "identical keys, threshold", exact_counts=True)
