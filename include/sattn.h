@@ -289,8 +289,8 @@ int sattn_vsmooth_quantize(const void* v, int B, int H, int Nk, int D, uint8_t* 
  * Range: the sums are kept in the frame of the row's first reference point, each later block scaled
  * by 2^(m - m_first) with that factor capped at 2^90 so the fp32 sums stay finite.  A row whose
  * largest listed score exceeds m_first by more than 90 log2 units (62.38 in units of scale q.k)
- * weighs its later keys as if the excess were 90 log2 units; no error is reported for it.  Rows
- * within that range get the result above.
+ * would weigh its later keys wrongly, so its out and lse are written as NaN (the call still returns
+ * SATTN_OK).  Rows within that range get the result above.
  * Errors: as sattn_forward; codes, vscale and vmean must be 16-byte aligned.
  */
 int sattn_fp8_forward(const void* q, const void* k, const uint8_t* codes, const float* vscale,

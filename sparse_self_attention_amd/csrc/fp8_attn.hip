@@ -30,7 +30,8 @@
 //    in the frame of the row's first reference point and each product takes its row's 2^(m - m0)
 //    through the per-lane E8M0 B scale of v_mfma_scale_f32_32x32x64_f8f6f4 (exact).  The scale is
 //    capped at 2^90 (the fp32 sums stay finite): a row whose max grows by more than 90 log2 units past
-//    its first block weighs its later blocks as if it had grown by 90.
+//    its first block would weigh its later blocks as if it had grown by 90, so its out and lse are
+//    written as NaN instead.
 //  * O^T += V8^T P^T: A = the V codes read from LDS with ds_read_b64_tr_b8 (the gfx950 transposing
 //    byte read), four 8-byte reads per 64-key tile and 32 output dims.  Rows are XOR-swizzled in
 //    32-byte pairs so the eight rows of one transposing read hit distinct banks.
@@ -724,7 +725,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
   if (nblk > 0) flush();
 
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  // a row whose point grew past the frame's range (F8_MAX_GROWTH) has weighed its later keys wrongly:
+  // its out and lse are NaN rather than a wrong number
+  const bool over_range = (m8 - mbase8) * 0.125f > (float)F8_MAX_GROWTH;
+  const float inv = over_range ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
   if (row_valid) {
     const size_t orow = ((size_t)bh * Nq + r0 + wrow) * D;
     const float* sc = vscale + (size_t)bh * D;
@@ -741,7 +745,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(F8Layou
       }
     if (lse != nullptr && hi == 0)
       lse[(size_t)bh * Nq + r0 + wrow] =
-          l_tot > 0.0f ? (mbase8 * 0.125f - 8.0f + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+          over_range ? __builtin_nanf("")
+                     : l_tot > 0.0f ? (mbase8 * 0.125f - 8.0f + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
 }
 

@@ -264,3 +264,35 @@ def test_fp8_scores_rising_close_to_the_range_limit(sattn):
     eo, el = oracle.sparse_attention_ref(f64(qb), f64(kb), vhat, idx, counts, group, scale)
     check_expcast_bound(out.cpu().numpy(), lse.cpu().numpy(), eo, el, value_ranges(vhat, idx, counts, group, Nq),
                         "scores near the range limit vs exact softmax", mean_abs_max=float(np.abs(rm).max()))
+
+
+def test_fp8_rows_past_the_range_are_nan(sattn):
+    """A key ~104 log2 units above the first block's maximum for half of the rows (past the 90-unit frame
+    range: their out and lse must be NaN) and ~78 units above it for the other half (inside the range:
+    the oracle's result)."""
+    rng = np.random.default_rng(104)
+    D, group, Nq, Nk = 64, 32, 32, 512
+    q = np.zeros((1, 1, Nq, D), dtype=np.float32)
+    q[0, 0, :16, 0], q[0, 0, 16:, 0] = 8.0, 6.0
+    q[..., 1:] = 0.25 * rng.standard_normal((1, 1, Nq, D - 1))
+    k = rng.standard_normal((1, 1, Nk, D)).astype(np.float32)
+    k[0, 0, 300, 0] = 72.0
+    qb, kb = inputs.f32_to_bf16_bits(q), inputs.f32_to_bf16_bits(k)
+    vb = inputs.f32_to_bf16_bits(rng.standard_normal((1, 1, Nk, D)).astype(np.float32))
+    idx = np.arange(Nk, dtype=np.int32)[None, None, None, :]
+    counts = np.full((1, 1, 1), Nk, dtype=np.int32)
+    scale = scale_of(D)
+    s2 = (f64(qb)[0, 0] @ f64(kb)[0, 0].T) * scale / np.log(2.0)
+    growth = s2.max(axis=1) - np.ceil(8.0 * s2[:, :64].max(axis=1)) / 8.0
+    assert growth[:16].min() > 91.0 and growth[16:].max() < 89.0
+    rc, rs, rm = oracle.vsmooth_quantize_ref(f64(vb))
+    codes, vscale, vmean = vsmooth_to_device(rc, rs, rm, Nk)
+    out, lse = sattn.fp8_forward(to_device_bf16(qb, DEV), to_device_bf16(kb, DEV), codes, vscale, vmean,
+                                 torch.from_numpy(idx).to(DEV), torch.from_numpy(counts).to(DEV), group,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isnan(out[0, 0, :16])) and np.all(np.isnan(lse[0, 0, :16]))
+    ref = oracle.fp8_attention_ref(f64(qb)[:, :, 16:], f64(kb), rc, rs, rm, idx, counts, group, scale,
+                                   tie_rel=fp8_tie_rel(D))
+    check_fp8_path(out[:, :, 16:], lse[:, :, 16:], ref, rm, "rows inside the range")
