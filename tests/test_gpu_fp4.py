@@ -229,3 +229,37 @@ def test_fp4_full_size_exact_softmax(sattn):
                                                    f"long_70200 fp4 h={h} g={g} vs exact softmax",
                                                    mean_abs_max=mean_max))
     print(f"long_70200 FP4-score forward: worst |out - exact| at {worst:.3f} of the ExpCast bound")
+
+
+def test_fp4_rows_past_the_range_are_nan(sattn):
+    """The 4-bit-score forward shares the FP8 frame: rows whose dequantised scores grow more than 90 log2
+    units past the first block get NaN out and lse, the other rows of the same group the oracle's result."""
+    rng = np.random.default_rng(135)
+    D, group, Nq, Nk = 64, 32, 32, 512
+    q = np.zeros((1, 1, Nq, D), dtype=np.float32)
+    q[0, 0, :16, 0], q[0, 0, 16:, 0] = 8.0, 4.0
+    q[..., 1:] = 0.25 * rng.standard_normal((1, 1, Nq, D - 1))
+    k = rng.standard_normal((1, 1, Nk, D)).astype(np.float32)
+    k[0, 0, 300, 0] = 90.0
+    qb, kb = inputs.f32_to_bf16_bits(q), inputs.f32_to_bf16_bits(k)
+    vb = inputs.f32_to_bf16_bits(rng.standard_normal((1, 1, Nk, D)).astype(np.float32))
+    idx = np.arange(Nk, dtype=np.int32)[None, None, None, :]
+    counts = np.full((1, 1, 1), Nk, dtype=np.int32)
+    scale = scale_of(D)
+    qc, qe = oracle.mx4_quantize_ref(f64(qb))
+    kc, ke = oracle.mx4_quantize_ref(f64(kb))
+    s2 = (oracle.mx4_dequantize_ref(qc, qe)[0, 0] @ oracle.mx4_dequantize_ref(kc, ke)[0, 0].T) * scale / np.log(2.0)
+    growth = s2.max(axis=1) - np.ceil(8.0 * s2[:, :64].max(axis=1)) / 8.0
+    assert growth[:16].min() > 91.0 and growth[16:].max() < 89.0
+    vc, vs, vm = oracle.vsmooth_quantize_ref(f64(vb))
+    q4, qs = (torch.from_numpy(a).to(DEV) for a in _pack(qc, qe))
+    k4, ks = (torch.from_numpy(a).to(DEV) for a in _pack(kc, ke))
+    codes, vscale, vmean = vsmooth_to_device(vc, vs, vm, Nk)
+    out, lse = sattn.fp4_forward(q4, qs, k4, ks, codes, vscale, vmean, torch.from_numpy(idx).to(DEV),
+                                 torch.from_numpy(counts).to(DEV), group, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isnan(out[0, 0, :16])) and np.all(np.isnan(lse[0, 0, :16]))
+    ref = oracle.fp4_attention_ref(qc[:, :, 16:], qe[:, :, 16:], kc, ke, vc, vs, vm, idx, counts, group, scale,
+                                   tie_rel=fp8_tie_rel(D))
+    check_fp8_path(out[:, :, 16:], lse[:, :, 16:], ref, vm, "4-bit scores, rows inside the range")
